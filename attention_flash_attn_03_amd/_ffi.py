@@ -1,0 +1,94 @@
+"""ctypes mirror of include/attn.h and loader for the in-tree libattn.so.
+
+Loading fails loudly when the library has not been built: there is no other
+implementation behind the binding.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libattn.so")
+
+ATTN_OK, ATTN_EINVAL, ATTN_EHIP = 0, 1, 2
+ATTN_NONE, ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2, 3
+ATTN_KV_TILE = 64
+
+_i32, _i64, _u32, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float
+_vp, _sz = ctypes.c_void_p, ctypes.c_size_t
+
+
+class PrefillParams(ctypes.Structure):
+    _fields_ = (
+        [(n, _i32) for n in ("batch", "rows", "kv_len", "n_heads", "n_kv_heads", "head_dim",
+                             "q_dtype", "kv_dtype", "mask_dtype")]
+        + [("scale", _f32)]
+        + [(n, _i64) for n in ("q_bs", "q_rs", "q_hs", "k_bs", "k_rs", "k_hs", "v_bs", "v_rs", "v_hs",
+                               "m_bs", "m_hs", "m_rs", "o_bs", "o_rs", "o_hs",
+                               "q_cap", "k_cap", "v_cap", "m_cap", "o_cap")]
+    )
+
+
+class DecodeParams(ctypes.Structure):
+    _fields_ = (
+        [(n, _i32) for n in ("batch", "n_heads", "n_kv_heads", "head_dim", "page_size", "max_pages_per_seq",
+                             "num_pages", "max_context", "kv_dtype")]
+        + [("scale", _f32)]
+        + [(n, _i64) for n in ("q_bs", "q_hs", "o_bs", "o_hs", "kv_page_stride", "kv_token_stride",
+                               "kv_head_stride", "q_cap", "kv_cap", "o_cap")]
+    )
+
+
+class DFlashParams(ctypes.Structure):
+    _fields_ = [(n, _u32) for n in ("lanes", "q_heads", "kv_heads", "head_dim", "rows", "window",
+                                    "packed_len", "max_commit")]
+
+
+# every function the header declares, with its ctypes signature
+SIGNATURES = {
+    "attn_last_error": ([], ctypes.c_char_p),
+    "attn_kv_pad": ([_u32], _u32),
+    "attn_prefill_workspace_bytes": ([ctypes.POINTER(PrefillParams), ctypes.POINTER(_sz)], ctypes.c_int),
+    "attn_prefill": ([ctypes.POINTER(PrefillParams), _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
+    "attn_paged_decode_workspace_bytes": ([ctypes.POINTER(DecodeParams), ctypes.POINTER(_sz)], ctypes.c_int),
+    "attn_paged_decode": ([ctypes.POINTER(DecodeParams), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+                          ctypes.c_int),
+    "dflash_validate": ([ctypes.POINTER(DFlashParams)], ctypes.c_int),
+    "dflash_pack": ([ctypes.POINTER(DFlashParams)] + [_vp] * 10 + [ctypes.POINTER(ctypes.c_uint64), _vp],
+                    ctypes.c_int),
+    "dflash_mask": ([ctypes.POINTER(DFlashParams), _vp, _vp, ctypes.POINTER(ctypes.c_uint64), _vp], ctypes.c_int),
+    "dflash_commit": ([ctypes.POINTER(DFlashParams)] + [_vp] * 6 + [ctypes.POINTER(ctypes.c_uint64), _vp],
+                      ctypes.c_int),
+    "dflash_mask_rows": ([_u32, _u32, _u32, _vp, _vp, ctypes.POINTER(ctypes.c_uint64), _vp], ctypes.c_int),
+}
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    """A non-OK status from libattn.so (the message is attn_last_error())."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__("[status %d] %s" % (status, message))
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libattn.so is not built (%s); run `python -m attention_flash_attn_03_amd._build` "
+                              "or __graft_entry__.build()" % LIB_PATH)
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (args, res) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = handle
+    return _lib
+
+
+def check(status: int) -> None:
+    if status != ATTN_OK:
+        raise AttnError(status, lib().attn_last_error().decode(errors="replace"))

@@ -1,0 +1,61 @@
+// device_common.h -- small device helpers shared by the gfx950 kernels:
+// vector types, 16-bit float conversions and wavefront reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bhalf8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef float float16v __attribute__((ext_vector_type(16)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef uint32_t uint4v __attribute__((ext_vector_type(4)));
+
+// f32 -> bf16 bits, round to nearest with ties to even; NaN stays NaN with
+// its quiet bit set; overflow rounds to infinity; subnormals are kept.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+    return __uint_as_float((uint32_t)b << 16);
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// Pack two 16-bit patterns into one dword (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack2(uint16_t lo, uint16_t hi) {
+    return (uint32_t)lo | ((uint32_t)hi << 16);
+}
+
+// Exchange with the lane 32 positions away: returns {x[l], x[l^32]} in an
+// order that depends on the half; max/sum of the pair is symmetric.
+__device__ __forceinline__ float max_with_other_half(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_with_other_half(float x) {
+    auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Sum over the 16 lanes of a row (lanes 16k..16k+15); every lane gets the sum.
+// DPP: swap neighbours, swap pairs, mirror within 8, mirror within 16.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(x), 0xB1, 0xF, 0xF, true));  // quad_perm 1,0,3,2
+    x += __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(x), 0x4E, 0xF, 0xF, true));  // quad_perm 2,3,0,1
+    x += __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(x), 0x141, 0xF, 0xF, true)); // row_half_mirror
+    x += __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(x), 0x140, 0xF, 0xF, true)); // row_mirror
+    return x;
+}
+
+}  // namespace attn

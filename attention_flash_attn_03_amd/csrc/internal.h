@@ -1,0 +1,67 @@
+// internal.h -- launch plans and launcher declarations shared between the
+// C-ABI layer (api.cpp) and the kernel files.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/attn.h"
+
+namespace attn {
+
+// Tile classification codes, one byte per (workgroup query block, 64-key tile).
+enum : uint8_t { TILE_SKIP = 0, TILE_MASKED = 1, TILE_OPEN = 2 };
+
+// How one attn_prefill call is cut into workgroups.  A workgroup owns one
+// batch item, one KV head, `heads_per_wg` consecutive query heads of that KV
+// head and `rows_per_wg` consecutive query rows: rows_per_wg * heads_per_wg
+// query slots, 32 per query wave.  Its waves split the head dimension into
+// `slices` slices of at most 256 columns.
+struct PrefillPlan {
+    int head_dim, slices, slice_dim;
+    int rows_per_wg, heads_per_wg, query_waves, waves;
+    int row_blocks, head_groups;      // per batch item: ceil(rows/rows_per_wg), n_kv_heads * g / heads_per_wg
+    int kv_tiles;                     // ceil(kv_len / 64)
+    int splits, tiles_per_split;      // KV range split across workgroups
+    size_t blk_bytes, blk_offset;     // tile codes [batch][head_groups][row_blocks][kv_tiles]
+    size_t part_offset, part_bytes;   // split partials: O [splits][batch][n_heads][rows][D] f32
+    size_t ml_offset, ml_bytes;       // split partials: (m, l) [splits][batch][n_heads][rows] float2
+    size_t workspace_bytes;
+};
+
+int plan_prefill(const attn_prefill_params *p, PrefillPlan *plan);
+hipError_t launch_prefill(const attn_prefill_params *p, const PrefillPlan *plan, const void *q,
+                          const void *k, const void *v, const void *mask, float *o, void *ws,
+                          hipStream_t stream);
+
+struct DecodePlan {
+    int head_dim, group;              // query heads per KV head
+    int heads_per_wg;                 // query heads one workgroup serves
+    int chunk;                        // tokens per split
+    int max_splits;
+    size_t part_offset, part_bytes;   // O partials [batch][n_heads][max_splits][D] f32
+    size_t ml_offset, ml_bytes;       // (m, l) [batch][n_heads][max_splits] float2
+    size_t workspace_bytes;
+};
+
+int plan_decode(const attn_decode_params *p, DecodePlan *plan);
+hipError_t launch_paged_decode(const attn_decode_params *p, const DecodePlan *plan, const float *q,
+                               const void *k_pool, const void *v_pool, const int32_t *page_table,
+                               const int32_t *context_lens, float *o, void *ws, hipStream_t stream);
+
+hipError_t launch_dflash_pack(const dflash_params *p, const uint16_t *ring_k, const uint16_t *ring_v,
+                              const float *cur_q, const float *cur_k, const float *cur_v,
+                              const uint32_t *cache_lengths, const uint32_t *write_positions,
+                              uint16_t *packed_q, uint16_t *packed_k, uint16_t *packed_v,
+                              hipStream_t stream);
+hipError_t launch_dflash_mask(const dflash_params *p, const uint32_t *cache_lengths, uint16_t *mask,
+                              hipStream_t stream);
+hipError_t launch_dflash_commit(const dflash_params *p, const float *new_k, const float *new_v,
+                                const uint32_t *commit_counts, const uint32_t *write_positions,
+                                uint16_t *ring_k, uint16_t *ring_v, hipStream_t stream);
+hipError_t launch_dflash_mask_rows(uint32_t lanes, uint32_t rows, uint32_t hidden,
+                                   const uint16_t *mask_embedding, float *draft_input,
+                                   hipStream_t stream);
+
+}  // namespace attn

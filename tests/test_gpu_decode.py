@@ -1,0 +1,107 @@
+"""GPU parity of attn_paged_decode against the fp64 oracle, elementwise within
+|err| <= 2e-3 * (1 + |ref|): oracle-sized page tables, bf16 and head_dim 256,
+empty contexts, NaN-poisoned unused slots, the interleaved K/V token record,
+paged == contiguous (through attn_prefill), and the full-size paged-decode
+configuration (64 sequences, contexts 512..16384, 65536-page pool) checked on
+sampled sequences in the benchmark's launch configuration."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attention_flash_attn_03_amd as fa
+import workloads
+from gpu_util import announce, assert_close, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(case, k_pool=None, v_pool=None, max_context=None):
+    bf = case.meta["kv_dtype"] == "bf16"
+    q = dev(case.q)
+    kp = dev(case.k_pool, bf) if k_pool is None else k_pool
+    vp = dev(case.v_pool, bf) if v_pool is None else v_pool
+    out = torch.full(case.q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    fa.attn_paged_decode(q, kp, vp, dev(case.page_table), dev(case.context_lens), out, scale=case.scale,
+                         max_context=case.max_context if max_context is None else max_context)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _oracle(orc, case, seqs=None):
+    sel = slice(None) if seqs is None else seqs
+    return orc.paged_decode(case.q[sel], case.k_pool, case.v_pool, case.page_table[sel], case.context_lens[sel],
+                            scale=case.scale, kv_bf16=case.meta["kv_dtype"] == "bf16")
+
+
+@pytest.mark.parametrize("kw", [
+    dict(batch=6, ctx_lo=1, ctx_hi=700, num_pages=300, n_heads=8, n_kv_heads=2, head_dim=128, seed=31),
+    dict(batch=4, ctx_lo=100, ctx_hi=3000, num_pages=800, n_heads=4, n_kv_heads=4, head_dim=128, seed=32),
+    dict(batch=3, ctx_lo=1, ctx_hi=900, num_pages=200, n_heads=8, n_kv_heads=1, head_dim=256, seed=33,
+         kv_dtype="bf16"),
+    dict(batch=5, ctx_lo=5000, ctx_hi=9000, num_pages=3000, n_heads=16, n_kv_heads=2, head_dim=128, seed=34),
+])
+def test_decode_oracle_sized(orc, kw):
+    announce("decode %s" % kw)
+    case = workloads.paged_case(**kw)
+    assert_close(_run(case), _oracle(orc, case), "decode")
+
+
+def test_empty_and_one_token_contexts(orc):
+    announce("decode empty contexts")
+    case = workloads.paged_case(batch=4, num_pages=64, n_heads=4, n_kv_heads=2, head_dim=128, seed=35,
+                                ctx_hi=100, context_lens=np.array([0, 1, 17, 0], np.int32))
+    got = _run(case)
+    assert np.all(got[[0, 3]] == 0.0)
+    assert_close(got, _oracle(orc, case), "decode short")
+
+
+def test_poisoned_unused_slots_are_never_read(orc):
+    announce("decode NaN-poisoned unused slots")
+    kw = dict(batch=5, ctx_lo=1, ctx_hi=400, num_pages=200, n_heads=8, n_kv_heads=2, head_dim=128, seed=36)
+    clean = workloads.paged_case(**kw)
+    poisoned = workloads.paged_case(poison_unused=True, **kw)
+    a, b = _run(clean), _run(poisoned)
+    assert np.all(np.isfinite(b))
+    assert np.array_equal(a, b)
+
+
+def test_interleaved_token_record(orc):
+    """The token record [2 (K, V), kv_heads, head_dim] of one pool: k_pool = base,
+    v_pool = base + kv_heads*head_dim, token stride 2*kv_heads*head_dim."""
+    announce("decode interleaved K/V record")
+    case = workloads.paged_case(batch=3, ctx_lo=10, ctx_hi=300, num_pages=80, n_heads=4, n_kv_heads=2, head_dim=128,
+                                seed=37)
+    rec = np.stack([case.k_pool, case.v_pool], axis=2)          # [pages, slot, 2, hk, d]
+    base = dev(rec)
+    kview = base[:, :, 0]
+    vview = base[:, :, 1]
+    assert kview.stride() == vview.stride()
+    got = _run(case, k_pool=kview, v_pool=vview)
+    assert_close(got, _oracle(orc, case), "interleaved")
+
+
+def test_paged_equals_contiguous_prefill(orc):
+    announce("decode paged vs contiguous prefill")
+    case = workloads.paged_case(batch=3, ctx_lo=200, ctx_hi=600, num_pages=200, n_heads=8, n_kv_heads=2,
+                                head_dim=128, seed=38)
+    paged = _run(case)
+    for b in range(3):
+        n = int(case.context_lens[b])
+        t = np.arange(n)
+        kk = case.k_pool[case.page_table[b, t // 16], t % 16][None]
+        vv = case.v_pool[case.page_table[b, t // 16], t % 16][None]
+        out = torch.zeros((1, 1, 8, 128), dtype=torch.float32, device="cuda")
+        fa.attn_prefill(dev(case.q[b][None, None]), dev(kk), dev(vv), None, out, scale=case.scale)
+        torch.cuda.synchronize()
+        assert_close(paged[b], out.cpu().numpy()[0, 0].astype(np.float64), "paged vs contiguous", tol=1e-4)
+
+
+def test_full_size_config_sampled(orc):
+    announce("decode full size (64 seqs, 65536-page pool), sampled sequences")
+    case = workloads.paged_case()
+    got = _run(case)
+    order = np.argsort(case.context_lens)
+    seqs = np.unique(np.concatenate([order[:2], order[-2:], [7, 31, 50]]))
+    assert_close(got[seqs], _oracle(orc, case, seqs), "decode full size")
