@@ -111,7 +111,9 @@ int check_prefill(const attn_prefill_params *p, attn::PrefillPlan *plan) {
         need > p->o_cap)
         return fail("attn_prefill: out holds %lld elements, the strides need more %s", (long long)p->o_cap, d);
     if (attn::plan_prefill(p, plan) != ATTN_OK) return fail("attn_prefill: no launch shape fits %s", d);
-    if (plan->head_groups > kMaxGridYZ || (int64_t)p->batch * plan->splits > kMaxGridYZ)
+    const int64_t blk_heads = (p->mask_dtype != ATTN_NONE && p->m_hs != 0) ? plan->head_groups : 1;
+    if (plan->head_groups > kMaxGridYZ || (int64_t)p->batch * plan->splits > kMaxGridYZ ||
+        plan->row_blocks > kMaxGridYZ || (int64_t)p->batch * blk_heads > kMaxGridYZ)
         return fail("attn_prefill: grid too large %s", d);
     return ATTN_OK;
 }

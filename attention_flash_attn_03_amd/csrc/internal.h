@@ -16,15 +16,16 @@ enum : uint8_t { TILE_SKIP = 0, TILE_MASKED = 1, TILE_OPEN = 2 };
 // How one attn_prefill call is cut into workgroups.  A workgroup owns one
 // batch item, one KV head, `heads_per_wg` consecutive query heads of that KV
 // head and `rows_per_wg` consecutive query rows: rows_per_wg * heads_per_wg
-// query slots, 32 per query wave.  Its waves split the head dimension into
-// `slices` slices of at most 256 columns.
+// query slots, 32 per query wave; with head_dim 512 two waves share the 32
+// slots, one per 256-column slice of the head dimension.
 struct PrefillPlan {
     int head_dim, slices, slice_dim;
     int rows_per_wg, heads_per_wg, query_waves, waves;
     int row_blocks, head_groups;      // per batch item: ceil(rows/rows_per_wg), n_kv_heads * g / heads_per_wg
     int kv_tiles;                     // ceil(kv_len / 64)
+    int blk_stride;                   // bytes per row of tile codes (kv_tiles rounded up to 4)
     int splits, tiles_per_split;      // KV range split across workgroups
-    size_t blk_bytes, blk_offset;     // tile codes [batch][head_groups][row_blocks][kv_tiles]
+    size_t blk_bytes, blk_offset;     // tile codes [batch][blk heads][row_blocks][blk_stride]
     size_t part_offset, part_bytes;   // split partials: O [splits][batch][n_heads][rows][D] f32
     size_t ml_offset, ml_bytes;       // split partials: (m, l) [splits][batch][n_heads][rows] float2
     size_t workspace_bytes;

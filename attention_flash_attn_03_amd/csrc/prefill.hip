@@ -7,25 +7,27 @@
 // tile) blocks are classified beforehand so empty tiles are skipped.
 //
 // CDNA4 design (not the page's Metal design):
-//  * A wave owns 32 query slots (query row, head pairs of one KV head) and a
-//    slice of at most 256 head-dim columns.  It computes S^T = K Q^T with
+//  * A wave owns 32 query slots (query row, head pairs of one KV head) and the
+//    whole head dimension.  It computes S^T = K Q^T with
 //    v_mfma_f32_32x32x16_{f16,bf16}: the accumulator layout puts one query
 //    column in each lane (lane l holds query l%32 and 16 keys of a 32-key
 //    block), so row max / row sum are in-lane plus one permlane32 swap, and
-//    the rescale of the output is a per-lane scalar.
+//    the rescale of the output is a per-lane scalar.  O^T for head_dim 512
+//    lives in the 256 accumulation registers (one wave per SIMD).
 //  * O^T = V^T P^T reuses P^T straight from the S^T accumulator registers as
 //    the B operand; V stays row-major in LDS and its transposed A fragments
 //    come from ds_read_b64_tr_b16 (4 keys x 1 column per lane per read).
-//  * K and V tiles (64 rows) are staged in LDS with 128-bit loads; rows are
-//    padded so the 128-bit K reads and the transposing V reads are free of
-//    bank conflicts.  head_dim 512 splits the head dimension over two waves
-//    that add their partial scores through LDS.
+//  * K and V tiles (64 rows) stream into LDS with global_load_lds_dwordx4
+//    (no staging registers), XOR-swizzled so both LDS read patterns are free
+//    of bank conflicts.  The loads are offset by half a tile: K(j+1) lands
+//    while softmax and P V of tile j run, V(j+1) while S of tile j+1 runs.
 //  * exp2 with log2(e) folded into the score scale; P is rounded to the K/V
 //    type before P V and the running sum l is taken from the rounded P, so
 //    the rounding cancels in O / l.  O is rescaled only when some lane's
 //    running max moved (lazy rescale).
-//  * Optional KV split across workgroups with a log-sum-exp combine pass for
-//    calls with few query blocks (block verify).
+//  * Row blocks are dispatched longest first (causal frontiers make the last
+//    blocks the heaviest).  Optional KV split across workgroups with a
+//    log-sum-exp combine pass for calls with few query blocks (block verify).
 #include <math.h>
 
 #include "device_common.h"
@@ -39,14 +41,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 template <int D>
 struct Geo {
-    static constexpr int DS = D > 256 ? 256 : D;   // head-dim slice per wave
-    static constexpr int NS = D / DS;              // slices
-    static constexpr int KSTEPS = DS / 16;          // MFMA k-steps for S over a slice
-    static constexpr int DBLK = DS / 32;            // 32-column O blocks per wave
-    static constexpr int KSTRIDE = D + 8;           // LDS row stride (elements) of the K tile
-    static constexpr int VSTRIDE = D + 32;          // LDS row stride (elements) of the V tile
-    static constexpr int K_ELEMS = kTile * KSTRIDE;
-    static constexpr int V_ELEMS = kTile * VSTRIDE;
+    static constexpr int CH = D / 8;         // 16-byte chunks per K/V row
+    static constexpr int KSTEPS = D / 16;    // MFMA k-steps for S
+    static constexpr int DBLK = D / 32;      // 32-column O blocks per wave
+    static constexpr int TILE_ELEMS = kTile * D;
 };
 
 struct PrefillArgs {
@@ -58,7 +56,7 @@ struct PrefillArgs {
     int64_t q_bs, q_rs, q_hs, k_bs, k_rs, k_hs, v_bs, v_rs, v_hs, m_bs, m_hs, m_rs, o_bs, o_rs, o_hs;
     int batch, rows, kv_len, n_heads, group;
     int rows_per_wg, heads_per_wg, row_blocks, head_groups, blk_heads;
-    int kv_tiles, splits, tiles_per_split;
+    int kv_tiles, blk_stride, splits, tiles_per_split;
     int q_bf16, mask_bf16, mask_vec;
     float score_scale;  // scale * log2(e)
 };
@@ -93,29 +91,96 @@ __device__ __forceinline__ float from_kv16(uint16_t x) {
 }
 
 typedef __attribute__((address_space(3))) short4v lds_short4;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(1))) void global_void;
 
 __device__ __forceinline__ short4v read_tr16(const uint16_t *lds_ptr) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(lds_ptr));
 }
 
+// LDS tile layouts (64 rows x D, no padding).  Chunk = 16 bytes = 8 elements.
+//  K: logical chunk c of row r sits at physical chunk c ^ (r % 16); the S^T
+//     A-operand read (16 consecutive rows, one chunk) hits 16 distinct banks.
+//  V: logical chunk c of row r sits at physical chunk c ^ 4*(r % 4); the
+//     transposing read (4 consecutive rows x 4 chunks per 32 lanes) hits 16
+//     distinct bank groups.
+__device__ __forceinline__ int k_swz(int row) { return row & 15; }
+__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 2; }
+
+// Stream one 64-row tile of K or V into LDS with global_load_lds_dwordx4: a
+// wave-instruction fills 64 consecutive 16-byte LDS slots starting at M0, so
+// each lane fetches the global chunk that belongs in its slot.  Rows past
+// kv_len fetch row kv_len-1 (finite data; those keys are masked to -inf).
+// Every wave issues exactly NLD instructions; the explicit vmcnt waits below
+// count them.  The instruction is issued from inline asm so the compiler does
+// not treat every later LDS read as dependent on it (its conservative
+// vmcnt(0) would drain the prefetch of the other tile); its own waits for
+// other loads only get stricter, never weaker, from loads it cannot see.
+template <int D, int NW, bool IS_V>
+__device__ __forceinline__ void issue_tile(uint16_t *lds, const uint16_t *base, int64_t row_stride, int key0,
+                                           int kv_len, int wave, int lane) {
+    constexpr int CH = D / 8;
+    constexpr int NLD = kTile * CH / (64 * NW);
+    // recompute the per-lane addresses here instead of keeping 2*NLD of them live across the loop
+    asm volatile("" : "+v"(lane));
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void *)lds;
+#pragma unroll
+    for (int it = 0; it < NLD; ++it) {
+        const int slot0 = (it * NW + wave) * 64;
+        const int slot = slot0 + lane;
+        const int row = slot / CH;
+        const int pch = slot % CH;
+        const int ch = pch ^ (IS_V ? v_swz(row) : k_swz(row));
+        int grow = key0 + row;
+        grow = grow < kv_len ? grow : kv_len - 1;
+        const uint16_t *src = base + (int64_t)grow * row_stride + ch * 8;
+        const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base + slot0 * 16);
+        // M0 is a reserved register the compiler does not let inline asm clobber; nothing
+        // else in this kernel reads it (no movrel, sendmsg or LDS-DMA intrinsic), so writing
+        // it here is safe.
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory");
+    }
+}
+
+// Wait until at most N of this wave's vector-memory operations are in flight,
+// then meet the other waves.  Loads retire in order, so N = the count issued
+// after the ones we need.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void lds_done_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+typedef const __attribute__((address_space(4))) uint32_t const_u32;
+
 // QSPLIT: f32 Q against bf16 K/V.  bf16 keeps 8 significant bits, which
 // perturbs every score by about 2^-9 relative; Q is carried as hi + lo bf16
 // parts (about 16 significant bits) and both products go into S.
-template <int D, bool BF16, bool HAS_MASK, bool QSPLIT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_kernel(PrefillArgs a) {
+//
+// NW waves per workgroup; with head_dim 512 the waves pair up as two slices
+// of 256 head-dim columns over the same 32 query slots (NS = 2) and add their
+// partial scores through LDS; otherwise every wave has its own query slots.
+template <int D, int NW, bool BF16, bool HAS_MASK, bool QSPLIT>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_kernel(PrefillArgs a) {
     using G = Geo<D>;
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[G::K_ELEMS];
-    __shared__ __attribute__((aligned(16))) uint16_t v_lds[G::V_ELEMS];
+    constexpr int NS = D > 256 ? 2 : 1;       // head-dim slices
+    constexpr int DS = D / NS;                 // columns per wave
+    constexpr int KSTEPS = DS / 16;            // MFMA k-steps of S over a slice
+    constexpr int DBLK = DS / 32;              // 32-column O blocks per wave
+    constexpr int NLD = kTile * G::CH / (64 * NW);
+    __shared__ __attribute__((aligned(1024))) uint16_t k_lds[G::TILE_ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds[G::TILE_ELEMS];
+    __shared__ __attribute__((aligned(16))) float x_lds[NS > 1 ? NW * 2 * 16 * 64 : 1];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int nthreads = blockDim.x;
-    const int slice = wave % G::NS;
-    const int qwave = wave / G::NS;
+    const int slice = wave % NS;
+    const int qwave = wave / NS;
     const int half = lane >> 5;    // which 8-element k half of an MFMA operand this lane feeds
     const int col = lane & 31;     // query slot column inside the wave
 
-    const int rb = blockIdx.x;
+    // longest-first: with a causal frontier the last row blocks carry the most tiles
+    const int rb = a.row_blocks - 1 - (int)blockIdx.x;
     const int hg = blockIdx.y;
     const int b = blockIdx.z / a.splits;
     const int split = blockIdx.z % a.splits;
@@ -130,14 +195,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int row_c = row_ok ? row : a.rows - 1;
 
     // ---- Q fragment: B operand of S^T = K Q^T, k = slice*DS + 16*ks + 8*half + i
-    uint4v qf[G::KSTEPS];
-    uint4v qlo[QSPLIT ? G::KSTEPS : 1];
+    uint4v qf[KSTEPS];
+    uint4v qlo[QSPLIT ? KSTEPS : 1];
     {
-        const int dbase = slice * G::DS + 8 * half;
+        const int dbase = slice * DS + 8 * half;
         if (a.q_bf16) {
             const uint16_t *qp = (const uint16_t *)a.q + b * a.q_bs + (int64_t)row_c * a.q_rs + head * a.q_hs + dbase;
 #pragma unroll
-            for (int ks = 0; ks < G::KSTEPS; ++ks) {
+            for (int ks = 0; ks < KSTEPS; ++ks) {
                 uint4v raw = *reinterpret_cast<const uint4v *>(qp + 16 * ks);
                 if constexpr (BF16) {
                     qf[ks] = raw;
@@ -155,7 +220,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         } else {
             const float *qp = (const float *)a.q + b * a.q_bs + (int64_t)row_c * a.q_rs + head * a.q_hs + dbase;
 #pragma unroll
-            for (int ks = 0; ks < G::KSTEPS; ++ks) {
+            for (int ks = 0; ks < KSTEPS; ++ks) {
                 const float4v x0 = *reinterpret_cast<const float4v *>(qp + 16 * ks);
                 const float4v x1 = *reinterpret_cast<const float4v *>(qp + 16 * ks + 4);
                 uint4v cv;
@@ -180,7 +245,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
         if (!row_ok) {
 #pragma unroll
-            for (int ks = 0; ks < G::KSTEPS; ++ks) {
+            for (int ks = 0; ks < KSTEPS; ++ks) {
                 qf[ks] = uint4v{0u, 0u, 0u, 0u};
                 if constexpr (QSPLIT) qlo[ks] = qf[ks];
             }
@@ -192,9 +257,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         mrow = (const uint16_t *)a.mask + b * a.m_bs + head * a.m_hs + (int64_t)row_c * a.m_rs;
     }
 
-    float16v acc_o[G::DBLK];
+    float16v acc_o[DBLK];
 #pragma unroll
-    for (int db = 0; db < G::DBLK; ++db)
+    for (int db = 0; db < DBLK; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.f;
     float m_run = -INFINITY;  // running max of the log2-scaled scores
@@ -202,38 +267,74 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
     const uint16_t *kbase = (const uint16_t *)a.k + b * a.k_bs + kvh * a.k_hs;
     const uint16_t *vbase = (const uint16_t *)a.v + b * a.v_bs + kvh * a.v_hs;
-    const uint8_t *blk_row = nullptr;
+    // tile codes are read as dwords through the scalar cache (constant address space)
+    const_u32 *blk_row = nullptr;
     if constexpr (HAS_MASK) {
         const int bh = a.blk_heads == 1 ? 0 : hg;
-        blk_row = a.blk + (((int64_t)b * a.blk_heads + bh) * a.row_blocks + rb) * a.kv_tiles;
+        blk_row = (const_u32 *)(a.blk + (((int64_t)b * a.blk_heads + bh) * a.row_blocks + rb) * a.blk_stride);
     }
-
-    const int kt_begin = split * a.tiles_per_split;
-    int kt_end = kt_begin + a.tiles_per_split;
-    if (kt_end > a.kv_tiles) kt_end = a.kv_tiles;
-
-    constexpr int CHUNKS_PER_ROW = D / 8;
-    constexpr int TILE_CHUNKS = kTile * CHUNKS_PER_ROW;
-
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-        int code = TILE_OPEN;
-        if constexpr (HAS_MASK) code = blk_row[kt];
-        if (code == TILE_SKIP) continue;  // uniform over the workgroup
-        const int key0 = kt * kTile;
-
-        // ---- stage K and V rows key0..key0+63 (zero past kv_len)
-        for (int c = threadIdx.x; c < TILE_CHUNKS; c += nthreads) {
-            const int r = c / CHUNKS_PER_ROW;
-            const int cc = c % CHUNKS_PER_ROW;
-            uint4v kx = uint4v{0u, 0u, 0u, 0u}, vx = kx;
-            if (key0 + r < a.kv_len) {
-                kx = *reinterpret_cast<const uint4v *>(kbase + (int64_t)(key0 + r) * a.k_rs + cc * 8);
-                vx = *reinterpret_cast<const uint4v *>(vbase + (int64_t)(key0 + r) * a.v_rs + cc * 8);
-            }
-            *reinterpret_cast<uint4v *>(&k_lds[r * G::KSTRIDE + cc * 8]) = kx;
-            *reinterpret_cast<uint4v *>(&v_lds[r * G::VSTRIDE + cc * 8]) = vx;
+    auto tile_code = [&](int t) -> int {
+        if constexpr (HAS_MASK) {
+            return (int)((blk_row[t >> 2] >> (8 * (t & 3))) & 0xffu);
+        } else {
+            return TILE_OPEN;
         }
-        __syncthreads();
+    };
+    const int kt_begin = split * a.tiles_per_split;
+    const int kt_end = min(kt_begin + a.tiles_per_split, a.kv_tiles);
+    auto next_tile = [&](int from) {
+        int t = from;
+        while (t < kt_end && tile_code(t) == TILE_SKIP) ++t;
+        return t < kt_end ? t : kt_end;
+    };
+
+    // per-lane pieces of the transposing V read: row kb + j/4, logical chunk
+    // 4*db + 2*(g&1) + (j&3)/2 (plus the slice), element 4*(j&1) inside the chunk
+    const int g16 = lane >> 4, j16 = lane & 15;
+    const int v_rsub = 4 * (g16 >> 1) + (j16 >> 2);
+    const int v_lchunk0 = slice * (DS / 8) + 2 * (g16 & 1) + ((j16 & 3) >> 1);
+    const int v_inner = 4 * (j16 & 1);
+
+    int kt = next_tile(kt_begin);
+    if (kt < kt_end) {
+        issue_tile<D, NW, false>(k_lds, kbase, a.k_rs, kt * kTile, a.kv_len, wave, lane);
+        issue_tile<D, NW, true>(v_lds, vbase, a.v_rs, kt * kTile, a.kv_len, wave, lane);
+    }
+    while (kt < kt_end) {
+        const int code = tile_code(kt);
+        const int nxt = next_tile(kt + 1);
+        const int key0 = kt * kTile;
+        const bool full_tile = key0 + kTile <= a.kv_len;
+
+        wait_vm_barrier<NLD>();  // K(kt) is in LDS for every wave; V(kt) may still be landing
+
+        // raw mask values of this lane's 32 keys (key0 + 32*blk2 + 8*q4 + 4*half + e); with two
+        // slices only slice 0 adds the mask into its partial scores
+        uint2 mraw[2][4];
+        const bool use_mask = HAS_MASK && code == TILE_MASKED && slice == 0;
+        if constexpr (HAS_MASK) {
+            if (use_mask) {
+                if (a.mask_vec && full_tile) {
+#pragma unroll
+                    for (int blk2 = 0; blk2 < 2; ++blk2)
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4)
+                            mraw[blk2][q4] = *reinterpret_cast<const uint2 *>(mrow + key0 + 32 * blk2 + 8 * q4 + 4 * half);
+                } else {
+                    // any alignment, any tail: element loads from clamped (in-bounds) keys
+#pragma unroll
+                    for (int blk2 = 0; blk2 < 2; ++blk2)
+#pragma unroll
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            const int kf = key0 + 32 * blk2 + 8 * q4 + 4 * half;
+                            uint16_t m16[4];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) m16[e] = mrow[min(kf + e, a.kv_len - 1)];
+                            mraw[blk2][q4] = make_uint2(pack2(m16[0], m16[1]), pack2(m16[2], m16[3]));
+                        }
+                }
+            }
+        }
 
         // ---- S^T (64 keys x 32 queries) over this wave's head-dim slice
         float16v s[2];
@@ -241,65 +342,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         for (int blk2 = 0; blk2 < 2; ++blk2) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[blk2][r] = 0.f;
-            const uint16_t *krow = &k_lds[(blk2 * 32 + col) * G::KSTRIDE + slice * G::DS + 8 * half];
+            const int krow = blk2 * 32 + col;
+            const uint16_t *kr = &k_lds[krow * D];
 #pragma unroll
-            for (int ks = 0; ks < G::KSTEPS; ++ks) {
-                const uint4v kf = *reinterpret_cast<const uint4v *>(krow + 16 * ks);
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                const int lch = slice * (DS / 8) + 2 * ks + half;
+                const uint4v kf = *reinterpret_cast<const uint4v *>(kr + 8 * (lch ^ k_swz(krow)));
                 s[blk2] = mfma32<BF16>(kf, qf[ks], s[blk2]);
                 if constexpr (QSPLIT) s[blk2] = mfma32<BF16>(kf, qlo[ks], s[blk2]);
             }
         }
-        if constexpr (G::NS > 1) {
-            // add the other slice's partial scores, exchanged through the K tile's LDS
-            __syncthreads();
-            float *xch = reinterpret_cast<float *>(k_lds);
-#pragma unroll
-            for (int blk2 = 0; blk2 < 2; ++blk2)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) xch[((wave * 2 + blk2) * 16 + r) * 64 + lane] = s[blk2][r];
-            __syncthreads();
-            const int other = qwave * G::NS + (1 - slice);
-#pragma unroll
-            for (int blk2 = 0; blk2 < 2; ++blk2)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[blk2][r] += xch[((other * 2 + blk2) * 16 + r) * 64 + lane];
-        }
 
-        // ---- scale, mask, tail; this lane holds keys key0 + 32*blk2 + 8*(r/4) + 4*half + r%4
-        const bool full_tile = key0 + kTile <= a.kv_len;
+        // ---- scale and mask (consumed before the next K tile is requested, so waiting for the
+        // mask loads never waits on that prefetch); this lane holds keys key0 + 32*blk2 + 8*(r/4) + 4*half + r%4
 #pragma unroll
-        for (int blk2 = 0; blk2 < 2; ++blk2) {
+        for (int blk2 = 0; blk2 < 2; ++blk2)
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                const int kfirst = key0 + 32 * blk2 + 8 * q4 + 4 * half;
-                float mv[4] = {0.f, 0.f, 0.f, 0.f};
-                if constexpr (HAS_MASK) {
-                    if (code == TILE_MASKED) {
-                        if (a.mask_vec && (full_tile || kfirst + 4 <= a.kv_len)) {
-                            const uint2 raw = *reinterpret_cast<const uint2 *>(mrow + kfirst);
-                            const uint16_t m16[4] = {(uint16_t)(raw.x & 0xffffu), (uint16_t)(raw.x >> 16),
-                                                     (uint16_t)(raw.y & 0xffffu), (uint16_t)(raw.y >> 16)};
-#pragma unroll
-                            for (int e = 0; e < 4; ++e)
-                                mv[e] = a.mask_bf16 ? bf16_bits_to_f32(m16[e]) : f16_bits_to_f32(m16[e]);
-                        } else {
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                if (kfirst + e < a.kv_len) {
-                                    const uint16_t m16 = mrow[kfirst + e];
-                                    mv[e] = a.mask_bf16 ? bf16_bits_to_f32(m16) : f16_bits_to_f32(m16);
-                                }
-                            }
-                        }
-                    }
-                }
+            for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    float t = fmaf(s[blk2][4 * q4 + e], a.score_scale, mv[e] * kLog2e);
-                    if (!full_tile && kfirst + e >= a.kv_len) t = -INFINITY;
-                    s[blk2][4 * q4 + e] = t;
+                    float mvf = 0.f;
+                    if (use_mask) {
+                        const uint32_t word = e < 2 ? mraw[blk2][q4].x : mraw[blk2][q4].y;
+                        const uint16_t m16 = (uint16_t)(word >> (16 * (e & 1)));
+                        mvf = (a.mask_bf16 ? bf16_bits_to_f32(m16) : f16_bits_to_f32(m16)) * kLog2e;
+                    }
+                    s[blk2][4 * q4 + e] = fmaf(s[blk2][4 * q4 + e], a.score_scale, mvf);
                 }
-            }
+        if constexpr (NS > 1) {
+#pragma unroll
+            for (int blk2 = 0; blk2 < 2; ++blk2)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) x_lds[((wave * 2 + blk2) * 16 + r) * 64 + lane] = s[blk2][r];
+        }
+        lds_done_barrier();  // every wave is done with K(kt) (and has posted its partial scores)
+        if (nxt < kt_end) issue_tile<D, NW, false>(k_lds, kbase, a.k_rs, nxt * kTile, a.kv_len, wave, lane);
+        if constexpr (NS > 1) {
+            const int other = qwave * NS + (1 - slice);
+#pragma unroll
+            for (int blk2 = 0; blk2 < 2; ++blk2)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[blk2][r] += x_lds[((other * 2 + blk2) * 16 + r) * 64 + lane];
+        }
+        if (!full_tile) {
+#pragma unroll
+            for (int blk2 = 0; blk2 < 2; ++blk2)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (key0 + 32 * blk2 + 8 * (r >> 2) + 4 * half + (r & 3) >= a.kv_len) s[blk2][r] = -INFINITY;
         }
 
         // ---- online softmax for this lane's query (32 keys here, 32 in lane ^ 32)
@@ -333,9 +423,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         m_run = m_new;
         if (__ballot(alpha != 1.f)) {
 #pragma unroll
-            for (int db = 0; db < G::DBLK; ++db)
+            for (int db = 0; db < DBLK; ++db)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
+        }
+
+        // V(kt) landed for every wave (K(nxt) may still be in flight)
+        if (nxt < kt_end) {
+            wait_vm_barrier<NLD>();
+        } else {
+            wait_vm_barrier<0>();
         }
 
         // ---- O^T[d][query] += V^T[d][key] P^T[key][query]
@@ -343,39 +440,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // A 16-lane group g reads 4 keys x 16 columns per ds_read_b64_tr_b16: lane j of the
         // group points at row kb + j/4, columns c0 + 4*(j%4) .. +3; lane j receives
         // rows kb..kb+3 of column c0 + j.
-        {
-            const int g = lane >> 4;
-            const int j = lane & 15;
-            const int col0 = slice * G::DS + 16 * (g & 1) + 4 * (j & 3);
-            const int rsub = 4 * (g >> 1) + (j >> 2);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int blk2 = u >> 1, e = u & 1;
-                const int kb0 = 32 * blk2 + 16 * e + rsub;
+        for (int u = 0; u < 4; ++u) {
+            const int blk2 = u >> 1, e = u & 1;
+            const int r0 = 32 * blk2 + 16 * e + v_rsub;      // rows r0 (slots 0..3) and r0 + 8 (slots 4..7)
+            const uint16_t *vr0 = &v_lds[r0 * D + v_inner];
+            const uint16_t *vr1 = &v_lds[(r0 + 8) * D + v_inner];
+            const int sw0 = v_swz(r0), sw1 = v_swz(r0 + 8);
 #pragma unroll
-                for (int db = 0; db < G::DBLK; ++db) {
-                    const uint16_t *p0 = &v_lds[kb0 * G::VSTRIDE + col0 + 32 * db];
-                    const short4v lo = read_tr16(p0);
-                    const short4v hi = read_tr16(p0 + 8 * G::VSTRIDE);
-                    uint4v vf;
-                    vf[0] = pack2((uint16_t)lo[0], (uint16_t)lo[1]);
-                    vf[1] = pack2((uint16_t)lo[2], (uint16_t)lo[3]);
-                    vf[2] = pack2((uint16_t)hi[0], (uint16_t)hi[1]);
-                    vf[3] = pack2((uint16_t)hi[2], (uint16_t)hi[3]);
-                    acc_o[db] = mfma32<BF16>(vf, pb[u], acc_o[db]);
-                }
+            for (int db = 0; db < DBLK; ++db) {
+                const int lch = 4 * db + v_lchunk0;
+                const short4v lo = read_tr16(vr0 + 8 * (lch ^ sw0));
+                const short4v hi = read_tr16(vr1 + 8 * (lch ^ sw1));
+                uint4v vf;
+                vf[0] = pack2((uint16_t)lo[0], (uint16_t)lo[1]);
+                vf[1] = pack2((uint16_t)lo[2], (uint16_t)lo[3]);
+                vf[2] = pack2((uint16_t)hi[0], (uint16_t)hi[1]);
+                vf[3] = pack2((uint16_t)hi[2], (uint16_t)hi[3]);
+                acc_o[db] = mfma32<BF16>(vf, pb[u], acc_o[db]);
             }
         }
-        __syncthreads();
+        lds_done_barrier();  // every wave is done with V(kt)
+        if (nxt < kt_end) issue_tile<D, NW, true>(v_lds, vbase, a.v_rs, nxt * kTile, a.kv_len, wave, lane);
+        kt = nxt;
     }
 
     // ---- epilogue: this lane holds O^T columns query `col`, rows d = slice*DS + 32*db + 8*(r/4) + 4*half + r%4
     if (!row_ok) return;
     if (a.splits == 1) {
         const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-        float *orow = a.o + b * a.o_bs + (int64_t)row * a.o_rs + head * a.o_hs + slice * G::DS + 4 * half;
+        float *orow = a.o + b * a.o_bs + (int64_t)row * a.o_rs + head * a.o_hs + slice * DS + 4 * half;
 #pragma unroll
-        for (int db = 0; db < G::DBLK; ++db)
+        for (int db = 0; db < DBLK; ++db)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 float4v x;
@@ -385,9 +481,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
     } else {
         const int64_t unit = (((int64_t)split * a.batch + b) * a.n_heads + head) * a.rows + row;
-        float *prow = a.part + unit * D + slice * G::DS + 4 * half;
+        float *prow = a.part + unit * D + slice * DS + 4 * half;
 #pragma unroll
-        for (int db = 0; db < G::DBLK; ++db)
+        for (int db = 0; db < DBLK; ++db)
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 float4v x;
@@ -399,70 +495,68 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 }
 
-// One wave classifies one (query block, 64-key tile) at a time: TILE_SKIP when
-// every entry is -inf, TILE_OPEN when every entry is zero, else TILE_MASKED.
-// Only entries of real rows (< rows) and keys (< kv_len) are read.
+// One wave classifies one (query block, 64-key tile): TILE_SKIP when every
+// entry is -inf, TILE_OPEN when every entry is zero, else TILE_MASKED.  Only
+// entries of real rows (< rows) and keys (< kv_len) are read.  Grid:
+// (ceil(kv_tiles / 4), row_blocks, batch * blk_heads), four waves per block.
 __global__ __launch_bounds__(256) void classify_kernel(PrefillArgs a, uint8_t *blk) {
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int rb = blockIdx.x;
-    const int hg = blockIdx.y;  // < blk_heads
-    const int b = blockIdx.z;
+    const int kt = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (kt >= a.kv_tiles) return;
+    const int rb = blockIdx.y;
+    const int hg = blockIdx.z % a.blk_heads;
+    const int b = blockIdx.z / a.blk_heads;
     const int slots = a.rows_per_wg * (a.blk_heads == 1 ? 1 : a.heads_per_wg);
     const int h0 = hg * a.heads_per_wg;
     const uint16_t *mbase = (const uint16_t *)a.mask + b * a.m_bs;
-    uint8_t *out = blk + (((int64_t)b * a.blk_heads + hg) * a.row_blocks + rb) * a.kv_tiles;
     const uint16_t neg_inf = a.mask_bf16 ? 0xFF80u : 0xFC00u;
-    for (int kt = wave; kt < a.kv_tiles; kt += 4) {
-        const int key0 = kt * kTile;
-        bool any_visible = false, any_nonzero = false;
-        if (a.mask_vec) {
-            // 8 lanes per 64-key row, 8 keys (16 bytes when aligned, else 2 x 8 bytes) per lane
-            for (int s = lane >> 3; s < slots; s += 8) {
-                const int head = h0 + s / a.rows_per_wg;
-                const int row = rb * a.rows_per_wg + s % a.rows_per_wg;
-                if (row >= a.rows) continue;
-                const uint16_t *mr = mbase + head * a.m_hs + (int64_t)row * a.m_rs;
-                const int kf = key0 + 8 * (lane & 7);
+    const int key0 = kt * kTile;
+    bool any_visible = false, any_nonzero = false;
+    if (a.mask_vec) {
+        // 16 lanes per 64-key row, 4 keys (8 bytes) per lane, 4 rows per pass
+        const int k4 = key0 + 4 * (lane & 15);
+        for (int s = lane >> 4; s < slots; s += 4) {
+            const int head = h0 + s / a.rows_per_wg;
+            const int row = rb * a.rows_per_wg + s % a.rows_per_wg;
+            if (row >= a.rows) continue;
+            const uint16_t *mr = mbase + head * a.m_hs + (int64_t)row * a.m_rs;
+            if (k4 + 4 <= a.kv_len) {
+                const uint2 raw = *reinterpret_cast<const uint2 *>(mr + k4);
+                const uint16_t m16[4] = {(uint16_t)(raw.x & 0xffffu), (uint16_t)(raw.x >> 16),
+                                         (uint16_t)(raw.y & 0xffffu), (uint16_t)(raw.y >> 16)};
 #pragma unroll
-                for (int half4 = 0; half4 < 2; ++half4) {
-                    const int k4 = kf + 4 * half4;
-                    if (k4 + 4 <= a.kv_len) {
-                        const uint2 raw = *reinterpret_cast<const uint2 *>(mr + k4);
-                        const uint16_t m16[4] = {(uint16_t)(raw.x & 0xffffu), (uint16_t)(raw.x >> 16),
-                                                 (uint16_t)(raw.y & 0xffffu), (uint16_t)(raw.y >> 16)};
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            any_visible |= m16[e] != neg_inf;
-                            any_nonzero |= (m16[e] & 0x7fffu) != 0;
-                        }
-                    } else {
-                        for (int e = 0; e < 4; ++e) {
-                            if (k4 + e < a.kv_len) {
-                                const uint16_t m16 = mr[k4 + e];
-                                any_visible |= m16 != neg_inf;
-                                any_nonzero |= (m16 & 0x7fffu) != 0;
-                            }
-                        }
+                for (int e = 0; e < 4; ++e) {
+                    any_visible |= m16[e] != neg_inf;
+                    any_nonzero |= (m16[e] & 0x7fffu) != 0;
+                }
+            } else {
+                for (int e = 0; e < 4; ++e) {
+                    if (k4 + e < a.kv_len) {
+                        const uint16_t m16 = mr[k4 + e];
+                        any_visible |= m16 != neg_inf;
+                        any_nonzero |= (m16 & 0x7fffu) != 0;
                     }
                 }
             }
-        } else {
+        }
+    } else {
+        const int key = key0 + lane;
+        if (key < a.kv_len) {
             for (int s = 0; s < slots; ++s) {
                 const int head = h0 + s / a.rows_per_wg;
                 const int row = rb * a.rows_per_wg + s % a.rows_per_wg;
                 if (row >= a.rows) continue;
-                const int key = key0 + lane;
-                if (key < a.kv_len) {
-                    const uint16_t m16 = mbase[head * a.m_hs + (int64_t)row * a.m_rs + key];
-                    any_visible |= m16 != neg_inf;
-                    any_nonzero |= (m16 & 0x7fffu) != 0;
-                }
+                const uint16_t m16 = mbase[head * a.m_hs + (int64_t)row * a.m_rs + key];
+                any_visible |= m16 != neg_inf;
+                any_nonzero |= (m16 & 0x7fffu) != 0;
             }
         }
-        const bool vis = __ballot(any_visible) != 0;
-        const bool nz = __ballot(any_nonzero) != 0;
-        if (lane == 0) out[kt] = !vis ? TILE_SKIP : (nz ? TILE_MASKED : TILE_OPEN);
+    }
+    const bool vis = __ballot(any_visible) != 0;
+    const bool nz = __ballot(any_nonzero) != 0;
+    if (lane == 0) {
+        uint8_t *out = blk + (((int64_t)b * a.blk_heads + hg) * a.row_blocks + rb) * a.blk_stride;
+        out[kt] = !vis ? TILE_SKIP : (nz ? TILE_MASKED : TILE_OPEN);
     }
 }
 
@@ -497,17 +591,26 @@ __global__ __launch_bounds__(256) void combine_kernel(PrefillArgs a) {
     *reinterpret_cast<float4v *>(a.o + b * a.o_bs + (int64_t)row * a.o_rs + head * a.o_hs + 4 * d4) = acc * inv;
 }
 
-template <int D, bool BF16, bool HAS_MASK>
-hipError_t launch_typed(const PrefillArgs &a, const PrefillPlan *plan, hipStream_t stream) {
+template <int D, int NW, bool BF16, bool HAS_MASK>
+hipError_t launch_nw(const PrefillArgs &a, const PrefillPlan *plan, hipStream_t stream) {
     dim3 grid(plan->row_blocks, plan->head_groups, (unsigned)(a.batch * plan->splits));
     if constexpr (BF16) {
         if (!a.q_bf16) {
-            hipLaunchKernelGGL((prefill_kernel<D, true, HAS_MASK, true>), grid, dim3(64 * plan->waves), 0, stream, a);
+            hipLaunchKernelGGL((prefill_kernel<D, NW, true, HAS_MASK, true>), grid, dim3(64 * NW), 0, stream, a);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((prefill_kernel<D, BF16, HAS_MASK, false>), grid, dim3(64 * plan->waves), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<D, NW, BF16, HAS_MASK, false>), grid, dim3(64 * NW), 0, stream, a);
     return hipGetLastError();
+}
+
+template <int D, bool BF16, bool HAS_MASK>
+hipError_t launch_typed(const PrefillArgs &a, const PrefillPlan *plan, hipStream_t stream) {
+    if (plan->waves == 4) return launch_nw<D, 4, BF16, HAS_MASK>(a, plan, stream);
+    if constexpr (D <= 256) {
+        if (plan->waves == 2) return launch_nw<D, 2, BF16, HAS_MASK>(a, plan, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int D>
@@ -544,24 +647,26 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 int plan_prefill(const attn_prefill_params *p, PrefillPlan *plan) {
     const int D = p->head_dim;
     plan->head_dim = D;
-    plan->slice_dim = D > 256 ? 256 : D;
-    plan->slices = D / plan->slice_dim;
+    plan->slices = D > 256 ? 2 : 1;
+    plan->slice_dim = D / plan->slices;
     const int g = p->n_heads / p->n_kv_heads;
+    // 4 waves hold 128 query slots (64 with two head-dim slices); at least 64 slots
     const int max_slots = plan->slices == 1 ? 128 : 64;
     int rpw = pow2_at_least(p->rows < 32 ? p->rows : 32);
     int hpw = 1;  // a power of two, so rows_per_wg * heads_per_wg can reach a multiple of 32
     for (int d = 1; d <= g; d *= 2)
         if (g % d == 0 && rpw * d <= max_slots) hpw = d;
-    while ((rpw * hpw) % 32 != 0) rpw *= 2;
+    while ((rpw * hpw) % 64 != 0) rpw *= 2;
     while (rpw * hpw < max_slots && rpw < p->rows) rpw *= 2;
     plan->rows_per_wg = rpw;
     plan->heads_per_wg = hpw;
     plan->query_waves = rpw * hpw / 32;
     plan->waves = plan->query_waves * plan->slices;
-    if (plan->waves < 1 || plan->waves > 4) return ATTN_EINVAL;  // the kernel is built for at most 256 threads
+    if (plan->waves != 4 && !(plan->waves == 2 && plan->slices == 1)) return ATTN_EINVAL;
     plan->row_blocks = (p->rows + rpw - 1) / rpw;
     plan->head_groups = p->n_heads / hpw;
     plan->kv_tiles = (p->kv_len + kTile - 1) / kTile;
+    plan->blk_stride = (plan->kv_tiles + 3) & ~3;  // rows of tile codes are read as dwords
     const int64_t wgs = (int64_t)plan->row_blocks * plan->head_groups * p->batch;
     int splits = 1;
     if (wgs < 256 && plan->kv_tiles >= 4) {
@@ -575,7 +680,7 @@ int plan_prefill(const attn_prefill_params *p, PrefillPlan *plan) {
     size_t off = 0;
     if (p->mask_dtype != ATTN_NONE) {
         const int blk_heads = p->m_hs == 0 ? 1 : plan->head_groups;
-        plan->blk_bytes = (size_t)p->batch * blk_heads * plan->row_blocks * plan->kv_tiles;
+        plan->blk_bytes = (size_t)p->batch * blk_heads * plan->row_blocks * plan->blk_stride;
     } else {
         plan->blk_bytes = 0;
     }
@@ -624,6 +729,7 @@ hipError_t launch_prefill(const attn_prefill_params *p, const PrefillPlan *plan,
     a.head_groups = plan->head_groups;
     a.blk_heads = (p->mask_dtype != ATTN_NONE && p->m_hs != 0) ? plan->head_groups : 1;
     a.kv_tiles = plan->kv_tiles;
+    a.blk_stride = plan->blk_stride;
     a.splits = plan->splits;
     a.tiles_per_split = plan->tiles_per_split;
     a.q_bf16 = p->q_dtype == ATTN_BF16;
@@ -634,7 +740,7 @@ hipError_t launch_prefill(const attn_prefill_params *p, const PrefillPlan *plan,
     a.score_scale = p->scale * kLog2e;
 
     if (a.mask) {
-        dim3 grid(plan->row_blocks, a.blk_heads, p->batch);
+        dim3 grid((plan->kv_tiles + 3) / 4, plan->row_blocks, p->batch * a.blk_heads);
         hipLaunchKernelGGL(classify_kernel, grid, dim3(256), 0, stream, a, (uint8_t *)a.blk);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
