@@ -164,7 +164,7 @@ int check_decode(const attn_decode_params *p, attn::DecodePlan *plan) {
                     d);
     attn::plan_decode(p, plan);
     const int hsplit = plan->group / plan->heads_per_wg;
-    if ((int64_t)p->n_kv_heads * hsplit > kMaxGridYZ || p->batch > kMaxGridYZ)
+    if (plan->max_splits > kMaxGridYZ || p->batch > kMaxGridYZ || (int64_t)p->n_kv_heads * hsplit > (1ll << 31) - 1)
         return fail("attn_paged_decode: grid too large %s", d);
     return ATTN_OK;
 }

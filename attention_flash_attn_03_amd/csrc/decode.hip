@@ -6,19 +6,22 @@
 // h reads KV head h / (query_heads / key_value_heads); the context includes
 // the token the step wrote).
 //
-// Design: decode is bound by HBM reads of K and V, so the kernel maximises
-// bytes in flight rather than arithmetic rate.
+// Design: decode is bound by HBM reads of K and V; the kernel keeps enough
+// bytes in flight and keeps the arithmetic off the vector ALUs.
 //  * Split-KV: workgroup (split, KV head, sequence) walks `chunk` tokens of
-//    one sequence for all query heads of one KV head (the K/V rows are read
-//    once for the whole group), then a second kernel merges the splits with a
+//    one sequence for the query heads of one KV head (each K/V row is read
+//    once for all of them); a second kernel merges the splits with a
 //    log-sum-exp reduction.
-//  * Inside a workgroup, 16 groups of 16 lanes each walk their own tokens;
-//    one token row (head_dim f16) is spread over the 16 lanes of a group as
-//    128-bit loads, so a row of 256 bytes is one coalesced access.  Each
-//    group keeps its own online-softmax state; scores are reduced across the
-//    16 lanes with DPP row operations.  The 16 group states are merged in LDS
-//    at the end of the chunk.
-//  * Every lane has 2*TB row loads in flight per step (TB tokens, K and V).
+//  * The (up to 16) query heads of a KV head are the 16 columns of a
+//    v_mfma_f32_16x16x32 tile: S^T = K Q^T and O^T = V^T P^T run on the
+//    matrix cores; P^T goes from the S^T accumulators straight into the
+//    B operand, and V^T fragments come from ds_read_b64_tr_b16.
+//  * Each wave streams its own 32-token K and V tiles into a private,
+//    double-buffered LDS region with global_load_lds_dwordx4 (the next tile
+//    is in flight while the current one is used), XOR-swizzled so the MFMA
+//    operand reads are free of bank conflicts.  The chunk's page ids are
+//    read once into LDS.
+//  * The waves' states are merged in LDS at the end of the chunk.
 #include <math.h>
 
 #include "device_common.h"
@@ -28,8 +31,9 @@ namespace attn {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kThreads = 256;
-constexpr int kGroups = kThreads / 16;
+constexpr int kTok = 32;      // tokens per wave step
+constexpr int kMaxChunk = 1024;  // tokens per workgroup (split) at most
+constexpr int kPgCap = kMaxChunk + 2;             // page ids of one chunk, any page size
 
 struct DecodeArgs {
     const float *q;
@@ -39,14 +43,36 @@ struct DecodeArgs {
     float *part;
     float2 *ml;
     int64_t q_bs, q_hs, o_bs, o_hs, page_stride, token_stride, head_stride;
-    int batch, n_heads, group, heads_per_wg, page_size, max_pages, num_pages, ctx_cap;
+    int batch, n_heads, group, heads_per_wg, page_size, page_shift, max_pages, num_pages, ctx_cap;
     int chunk, max_splits;
     float score_scale;
 };
 
+typedef __attribute__((address_space(3))) short4v lds_short4;
+typedef __attribute__((address_space(3))) void lds_void;
+
 template <bool BF16>
-__device__ __forceinline__ float kv_to_f32(uint32_t word, int hi) {
-    const uint16_t x = hi ? (uint16_t)(word >> 16) : (uint16_t)(word & 0xffffu);
+__device__ __forceinline__ float4v mfma16(uint4v a, uint4v b, float4v c) {
+    if constexpr (BF16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bhalf8, a), __builtin_bit_cast(bhalf8, b),
+                                                       c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, b), c,
+                                                      0, 0, 0);
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ uint16_t to_kv16(float x) {
+    if constexpr (BF16) {
+        return f32_to_bf16_rne(x);
+    } else {
+        return __builtin_bit_cast(uint16_t, (_Float16)x);
+    }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float from_kv16(uint16_t x) {
     if constexpr (BF16) {
         return bf16_bits_to_f32(x);
     } else {
@@ -54,199 +80,329 @@ __device__ __forceinline__ float kv_to_f32(uint32_t word, int hi) {
     }
 }
 
+// (x[l], x[l ^ 16]) and (x[l], x[l ^ 32]) pairs; max and sum of a pair are symmetric
+__device__ __forceinline__ float max_over_rows(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    return max_with_other_half(x);
+}
+__device__ __forceinline__ float sum_over_rows(float x) {
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    return sum_with_other_half(x);
+}
+
 __device__ __forceinline__ int clamp_ctx(int c, int cap) { return c < 0 ? 0 : (c > cap ? cap : c); }
 
-template <int D, int GW, bool BF16>
-__global__ __launch_bounds__(kThreads) void decode_partial_kernel(DecodeArgs a) {
-    constexpr int VPL = D / 16;            // elements of a row per lane
-    constexpr int TB = D <= 128 ? 8 : 4;   // tokens per group per step
-    constexpr int W4 = VPL / 8;            // 128-bit words per lane per row
+__device__ __forceinline__ int page_of(const DecodeArgs &a, int t) {
+    return a.page_shift >= 0 ? (t >> a.page_shift) : t / a.page_size;
+}
 
-    const int split = blockIdx.x;
-    const int hsplit = a.group / GW;
-    const int kvh = blockIdx.y / hsplit;
-    const int head0 = kvh * a.group + (blockIdx.y % hsplit) * GW;
+// LDS tile layouts (32 token rows x D, chunks of 16 bytes):
+//  K: logical chunk c of row r at physical c ^ (r % 16)   (A-operand reads: 16 rows, one chunk)
+//  V: logical chunk c of row r at physical c ^ 2*(r % 8)   (transposing reads: 8 rows x 2 chunks)
+__device__ __forceinline__ int k_swz(int row) { return row & 15; }
+__device__ __forceinline__ int v_swz(int row) { return (row & 7) << 1; }
+
+// Wait until at most N of this wave's vector-memory operations are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Stream the K and V rows of tokens base..base+31 (clamped to t1-1) into one
+// LDS buffer pair of this wave.  Each global_load_lds_dwordx4 fills 64
+// consecutive 16-byte slots from M0; every call issues exactly 2*NLD of them.
+// Issued from inline asm so the compiler's own waits do not drain it (see
+// the explicit vmcnt waits in the kernel).  M0 is read only by these loads.
+template <int D>
+__device__ __forceinline__ void issue_kv(const DecodeArgs &a, uint16_t *k_tile, uint16_t *v_tile, const int *s_pg,
+                                        int pg0, int base, int t1, int64_t head_off, int lane) {
+    constexpr int CH = D / 8;
+    constexpr int NLD = kTok * CH / 64;
+    int64_t row_off[NLD];
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+        const int row = (i * 64 + lane) / CH;
+        int t = base + row;
+        t = t < t1 ? t : t1 - 1;
+        const int pg = page_of(a, t);
+        const int page = s_pg[pg - pg0];
+        row_off[i] = (int64_t)page * a.page_stride + (int64_t)(t - pg * a.page_size) * a.token_stride + head_off;
+    }
+    const uint32_t kb = (uint32_t)(uintptr_t)(lds_void *)k_tile;
+    const uint32_t vb = (uint32_t)(uintptr_t)(lds_void *)v_tile;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+        const int slot = i * 64 + lane;
+        const int row = slot / CH, pch = slot % CH;
+        const uint16_t *ksrc = a.k_pool + row_off[i] + 8 * (pch ^ k_swz(row));
+        const uint16_t *vsrc = a.v_pool + row_off[i] + 8 * (pch ^ v_swz(row));
+        const uint32_t mk = __builtin_amdgcn_readfirstlane(kb + i * 1024);
+        const uint32_t mv = __builtin_amdgcn_readfirstlane(vb + i * 1024);
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(mk), "v"(ksrc) : "memory");
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(mv), "v"(vsrc) : "memory");
+    }
+}
+
+template <int D, int NWD, bool BF16>
+__global__ __launch_bounds__(64 * NWD) void decode_partial_kernel(DecodeArgs a) {
+    constexpr int CH = D / 8;
+    constexpr int TILE = kTok * D;             // elements of one 32-token tile
+    constexpr int NLD = kTok * CH / 64;        // load instructions per tile per wave
+    constexpr int KSTEPS = D / 32;             // MFMA k-steps of S^T
+    constexpr int DBLK = D / 16;               // 16-row blocks of O^T
+    __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[NWD * 4 * TILE];   // [wave][buffer][K, V]
+    __shared__ int s_pg[kPgCap];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    // KV head is the fastest-varying workgroup index: the workgroups reading the
+    // slices of the same token records run side by side
+    const int split = blockIdx.y;
+    const int hsplit = a.group / a.heads_per_wg;
+    const int kvh = blockIdx.x / hsplit;
+    const int head0 = kvh * a.group + (blockIdx.x % hsplit) * a.heads_per_wg;
     const int b = blockIdx.z;
     const int ctx = clamp_ctx(a.context_lens[b], a.ctx_cap);
     const int t0 = split * a.chunk;
     const int64_t unit0 = (int64_t)b * a.n_heads + head0;
     if (t0 >= ctx) {
-        if (threadIdx.x < GW) a.ml[(unit0 + threadIdx.x) * a.max_splits + split] = make_float2(-INFINITY, 0.f);
+        if (threadIdx.x < a.heads_per_wg) a.ml[(unit0 + threadIdx.x) * a.max_splits + split] = make_float2(-INFINITY, 0.f);
         return;
     }
-    const int t1 = t0 + a.chunk < ctx ? t0 + a.chunk : ctx;
+    const int t1 = min(t0 + a.chunk, ctx);
 
-    const int grp = threadIdx.x >> 4;
-    const int sub = threadIdx.x & 15;
-
-    float q[GW][VPL];
-#pragma unroll
-    for (int hh = 0; hh < GW; ++hh) {
-        const float *qp = a.q + b * a.q_bs + (int64_t)(head0 + hh) * a.q_hs + sub * VPL;
-#pragma unroll
-        for (int i = 0; i < VPL; i += 4) {
-            const float4v x = *reinterpret_cast<const float4v *>(qp + i);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) q[hh][i + e] = x[e] * a.score_scale;
-        }
-    }
-    float m[GW], l[GW], o[GW][VPL];
-#pragma unroll
-    for (int hh = 0; hh < GW; ++hh) {
-        m[hh] = -INFINITY;
-        l[hh] = 0.f;
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) o[hh][i] = 0.f;
-    }
-
-    const int32_t *pt = a.page_table + (int64_t)b * a.max_pages;
-    const int64_t head_off = (int64_t)kvh * a.head_stride + sub * VPL;
-
-    for (int base = t0 + grp * TB; base < t1; base += kGroups * TB) {
-        uint4v kw[TB][W4], vw[TB][W4];
-#pragma unroll
-        for (int k = 0; k < TB; ++k) {
-            const int t = base + k;
-            if (t < t1) {
-                int page = pt[t / a.page_size];
-                page = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
-                const int64_t off = (int64_t)page * a.page_stride + (int64_t)(t % a.page_size) * a.token_stride + head_off;
-#pragma unroll
-                for (int w = 0; w < W4; ++w) {
-                    kw[k][w] = *reinterpret_cast<const uint4v *>(a.k_pool + off + 8 * w);
-                    vw[k][w] = *reinterpret_cast<const uint4v *>(a.v_pool + off + 8 * w);
-                }
-            } else {
-#pragma unroll
-                for (int w = 0; w < W4; ++w) {
-                    kw[k][w] = uint4v{0u, 0u, 0u, 0u};
-                    vw[k][w] = kw[k][w];
-                }
-            }
-        }
-        float sc[GW][TB];
-#pragma unroll
-        for (int k = 0; k < TB; ++k) {
-            float kf[VPL];
-#pragma unroll
-            for (int i = 0; i < VPL; ++i) kf[i] = kv_to_f32<BF16>(kw[k][i / 8][(i % 8) / 2], i & 1);
-#pragma unroll
-            for (int hh = 0; hh < GW; ++hh) {
-                float s = 0.f;
-#pragma unroll
-                for (int i = 0; i < VPL; ++i) s = fmaf(q[hh][i], kf[i], s);
-                s = row16_sum(s);
-                sc[hh][k] = base + k < t1 ? s : -INFINITY;
-            }
-        }
-#pragma unroll
-        for (int hh = 0; hh < GW; ++hh) {
-            float mx = m[hh];
-#pragma unroll
-            for (int k = 0; k < TB; ++k) mx = fmaxf(mx, sc[hh][k]);
-            const float alpha = exp2f(m[hh] - mx);  // mx is finite: the first token of this step is real
-            m[hh] = mx;
-            float p[TB];
-            float ps = 0.f;
-#pragma unroll
-            for (int k = 0; k < TB; ++k) {
-                p[k] = exp2f(sc[hh][k] - mx);
-                ps += p[k];
-            }
-            l[hh] = l[hh] * alpha + ps;
-#pragma unroll
-            for (int i = 0; i < VPL; ++i) o[hh][i] *= alpha;
-#pragma unroll
-            for (int k = 0; k < TB; ++k)
-#pragma unroll
-                for (int i = 0; i < VPL; ++i) o[hh][i] = fmaf(p[k], kv_to_f32<BF16>(vw[k][i / 8][(i % 8) / 2], i & 1), o[hh][i]);
-        }
-    }
-
-    // ---- merge the 16 group states of this workgroup through LDS
-    __shared__ float s_o[kGroups][GW][D];
-    __shared__ float s_ml[kGroups][GW][2];
-#pragma unroll
-    for (int hh = 0; hh < GW; ++hh) {
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) s_o[grp][hh][sub * VPL + i] = o[hh][i];
-        if (sub == 0) {
-            s_ml[grp][hh][0] = m[hh];
-            s_ml[grp][hh][1] = l[hh];
-        }
+    // page ids of this chunk (entries past the context are never read)
+    const int pg0 = page_of(a, t0);
+    const int npg = page_of(a, t1 - 1) - pg0 + 1;
+    for (int i = threadIdx.x; i < npg; i += blockDim.x) {
+        int page = a.page_table[(int64_t)b * a.max_pages + pg0 + i];
+        s_pg[i] = page < 0 ? 0 : (page >= a.num_pages ? a.num_pages - 1 : page);
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < GW * D; e += kThreads) {
-        const int hh = e / D, d = e % D;
+
+    // Q^T as the B operand of S^T = K Q^T: column = query slot (lane % 16), k = 32*ks + 8*(lane/16) + i
+    const int slot = lane & 15, g4 = lane >> 4;
+    const bool slot_ok = slot < a.heads_per_wg;
+    uint4v qf[KSTEPS];
+    uint4v qlo[BF16 ? KSTEPS : 1];
+    {
+        const float *qp = a.q + b * a.q_bs + (int64_t)(head0 + (slot_ok ? slot : 0)) * a.q_hs + 8 * g4;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            const float4v x0 = *reinterpret_cast<const float4v *>(qp + 32 * ks);
+            const float4v x1 = *reinterpret_cast<const float4v *>(qp + 32 * ks + 4);
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                x[e] = slot_ok ? x0[e] * a.score_scale : 0.f;
+                x[4 + e] = slot_ok ? x1[e] * a.score_scale : 0.f;
+            }
+            uint16_t h[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) h[e] = to_kv16<BF16>(x[e]);
+            qf[ks] = uint4v{pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7])};
+            if constexpr (BF16) {
+                // bf16 keeps 8 significant bits: carry the rest of Q in a second operand
+                uint16_t r[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) r[e] = f32_to_bf16_rne(x[e] - bf16_bits_to_f32(h[e]));
+                qlo[ks] = uint4v{pack2(r[0], r[1]), pack2(r[2], r[3]), pack2(r[4], r[5]), pack2(r[6], r[7])};
+            }
+        }
+    }
+
+    float4v acc[DBLK];
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db) acc[db] = float4v{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    uint16_t *wbase = kv_lds + wave * 4 * TILE;
+    const int64_t head_off = (int64_t)kvh * a.head_stride;
+    // per-lane pieces of the transposing V read: row kb + j/4, logical chunk 2*db + (j&3)/2, element 4*(j&1)
+    const int v_rsub = lane & 15;
+    int base = t0 + kTok * wave;
+    int buf = 0;
+    if (base < t1) issue_kv<D>(a, wbase, wbase + TILE, s_pg, pg0, base, t1, head_off, lane);
+    while (base < t1) {
+        const int nbase = base + kTok * NWD;
+        const bool has_next = nbase < t1;
+        if (has_next) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the other buffer's reads are done
+            uint16_t *nb = wbase + (buf ^ 1) * 2 * TILE;
+            issue_kv<D>(a, nb, nb + TILE, s_pg, pg0, nbase, t1, head_off, lane);
+            wait_vm<2 * NLD>();
+        } else {
+            wait_vm<0>();
+        }
+        const uint16_t *k_tile = wbase + buf * 2 * TILE;
+        const uint16_t *v_tile = k_tile + TILE;
+
+        // ---- S^T (32 tokens x 16 slots): lane holds slot `slot`, tokens 16*blk + 4*g4 + r
+        float4v s[2];
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            s[blk] = float4v{0.f, 0.f, 0.f, 0.f};
+            const int row = 16 * blk + (lane & 15);
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                const uint4v kf = *reinterpret_cast<const uint4v *>(k_tile + row * D + 8 * ((4 * ks + g4) ^ k_swz(row)));
+                s[blk] = mfma16<BF16>(kf, qf[ks], s[blk]);
+                if constexpr (BF16) s[blk] = mfma16<BF16>(kf, qlo[ks], s[blk]);
+            }
+        }
+        if (base + kTok > t1) {
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (base + 16 * blk + 4 * g4 + r >= t1) s[blk][r] = -INFINITY;
+        }
+
+        // ---- online softmax per slot (8 tokens here, the other 24 in lanes ^16, ^32, ^48)
+        float mx = -INFINITY;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[blk][r]);
+        mx = max_over_rows(mx);
+        const float m_new = fmaxf(m_run, mx);   // finite: token `base` is real
+        const float alpha = exp2f(m_run - m_new);
+        uint16_t p16[8];
+        float ps = 0.f;
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p16[4 * blk + r] = to_kv16<BF16>(exp2f(s[blk][r] - m_new));
+                ps += from_kv16<BF16>(p16[4 * blk + r]);
+            }
+        ps = sum_over_rows(ps);
+        l_run = l_run * alpha + ps;
+        m_run = m_new;
+        if (__ballot(alpha != 1.f)) {
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db) acc[db] *= alpha;
+        }
+        // P^T as the B operand: k slot i <-> token 4*g4 + i (i < 4) and 16 + 4*g4 + (i - 4)
+        const uint4v pb = uint4v{pack2(p16[0], p16[1]), pack2(p16[2], p16[3]), pack2(p16[4], p16[5]),
+                                 pack2(p16[6], p16[7])};
+
+        // ---- O^T[d][slot] += V^T[d][token] P^T[token][slot]
+        // A operand: row d = 16*db + lane%16, k slots as above.  A 16-lane group reads rows kb..kb+3
+        // (kb = 4*g4, then 16 + 4*g4) x 16 columns per ds_read_b64_tr_b16: lane j points at row
+        // kb + j/4, columns 16*db + 4*(j%4), and receives rows kb..kb+3 of column 16*db + j.
+        {
+            const int r0 = 4 * g4 + (v_rsub >> 2), r1 = r0 + 16;
+            const uint16_t *v0 = v_tile + r0 * D + 4 * (v_rsub & 1);
+            const uint16_t *v1 = v_tile + r1 * D + 4 * (v_rsub & 1);
+            const int c0 = (v_rsub & 3) >> 1;
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db) {
+                const int lch = 2 * db + c0;
+                const short4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(v0 + 8 * (lch ^ v_swz(r0))));
+                const short4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(v1 + 8 * (lch ^ v_swz(r1))));
+                const uint4v vf = uint4v{pack2((uint16_t)lo[0], (uint16_t)lo[1]), pack2((uint16_t)lo[2], (uint16_t)lo[3]),
+                                         pack2((uint16_t)hi[0], (uint16_t)hi[1]), pack2((uint16_t)hi[2], (uint16_t)hi[3])};
+                acc[db] = mfma16<BF16>(vf, pb, acc[db]);
+            }
+        }
+        base = nbase;
+        buf ^= 1;
+    }
+
+    // ---- merge the waves through LDS (the tiles are no longer needed)
+    __syncthreads();
+    float *s_o = reinterpret_cast<float *>(kv_lds);              // [wave][slot][D]
+    float2 *s_ml = reinterpret_cast<float2 *>(s_o + NWD * 16 * D);  // [wave][slot]
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+        *reinterpret_cast<float4v *>(s_o + (wave * 16 + slot) * D + 16 * db + 4 * g4) = acc[db];
+    if (g4 == 0) s_ml[wave * 16 + slot] = make_float2(m_run, l_run);
+    __syncthreads();
+    for (int e = threadIdx.x; e < a.heads_per_wg * D; e += blockDim.x) {
+        const int sl = e / D, d = e % D;
         float mmax = -INFINITY;
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g) mmax = fmaxf(mmax, s_ml[g][hh][0]);
-        float acc = 0.f, lsum = 0.f;
+        for (int w = 0; w < NWD; ++w) mmax = fmaxf(mmax, s_ml[w * 16 + sl].x);
+        float accv = 0.f, lsum = 0.f;
 #pragma unroll
-        for (int g = 0; g < kGroups; ++g) {
-            const float mg = s_ml[g][hh][0];
-            if (mg == -INFINITY) continue;  // group walked no token
-            const float w = exp2f(mg - mmax);
-            acc = fmaf(w, s_o[g][hh][d], acc);
-            lsum = fmaf(w, s_ml[g][hh][1], lsum);
+        for (int w = 0; w < NWD; ++w) {
+            const float2 ml = s_ml[w * 16 + sl];
+            if (ml.x == -INFINITY) continue;  // this wave walked no token
+            const float wgt = exp2f(ml.x - mmax);
+            accv = fmaf(wgt, s_o[(w * 16 + sl) * D + d], accv);
+            lsum = fmaf(wgt, ml.y, lsum);
         }
-        const int64_t u = (unit0 + hh) * a.max_splits + split;
-        a.part[u * D + d] = acc;
+        const int64_t u = (unit0 + sl) * a.max_splits + split;
+        a.part[u * D + d] = accv;
         if (d == 0) a.ml[u] = make_float2(mmax, lsum);
     }
 }
 
-// One thread per 4 output elements: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// One wave per (sequence, query head): O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
+// over the splits the sequence used.  Lanes read the (m, l) of 64 splits at a
+// time; the partials are streamed with coalesced loads.
 template <int D>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
-    constexpr int PER_UNIT = D / 4;
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int64_t unit = t / PER_UNIT;
-    const int d4 = t % PER_UNIT;
+    constexpr int PER_LANE = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (unit >= (int64_t)a.batch * a.n_heads) return;
     const int b = unit / a.n_heads, head = unit % a.n_heads;
     const int ctx = clamp_ctx(a.context_lens[b], a.ctx_cap);
     int nsplit = (ctx + a.chunk - 1) / a.chunk;
     if (nsplit > a.max_splits) nsplit = a.max_splits;
     const float2 *ml = a.ml + unit * a.max_splits;
+    const float *part = a.part + unit * a.max_splits * D;
+
     float mmax = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) mmax = fmaxf(mmax, ml[s].x);
-    float4v acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = lane; s < nsplit; s += 64) mmax = fmaxf(mmax, ml[s].x);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, off));
+
+    float o[PER_LANE];
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) o[i] = 0.f;
     float lsum = 0.f;
     if (mmax != -INFINITY) {
-        for (int s = 0; s < nsplit; ++s) {
-            if (ml[s].x == -INFINITY) continue;
-            const float w = exp2f(ml[s].x - mmax);
-            lsum += w * ml[s].y;
-            acc += w * *reinterpret_cast<const float4v *>(a.part + (unit * a.max_splits + s) * D + 4 * d4);
+        for (int s0 = 0; s0 < nsplit; s0 += 64) {
+            const int s = s0 + lane;
+            const float2 my = s < nsplit ? ml[s] : make_float2(-INFINITY, 0.f);
+            const float w = my.x == -INFINITY ? 0.f : exp2f(my.x - mmax);  // splits that saw no token weigh 0
+            float lw = w * my.y;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) lw += __shfl_xor(lw, off);
+            lsum += lw;
+            const int n = min(64, nsplit - s0);
+            for (int j = 0; j < n; ++j) {
+                const float wj = __shfl(w, j);
+                if (wj == 0.f) continue;
+                const float *pj = part + (int64_t)(s0 + j) * D + lane * PER_LANE;
+#pragma unroll
+                for (int i = 0; i < PER_LANE; ++i) o[i] = fmaf(wj, pj[i], o[i]);
+            }
         }
     }
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    *reinterpret_cast<float4v *>(a.o + b * a.o_bs + (int64_t)head * a.o_hs + 4 * d4) = acc * inv;
-}
-
-template <int D, int GW, bool BF16>
-hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
-    dim3 grid(a.max_splits, (a.n_heads / a.group) * (a.group / GW), a.batch);
-    hipLaunchKernelGGL((decode_partial_kernel<D, GW, BF16>), grid, dim3(kThreads), 0, stream, a);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    const int64_t threads = (int64_t)a.batch * a.n_heads * (D / 4);
-    hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, a);
-    return hipGetLastError();
+    float *orow = a.o + b * a.o_bs + (int64_t)head * a.o_hs + lane * PER_LANE;
+#pragma unroll
+    for (int i = 0; i < PER_LANE; ++i) orow[i] = o[i] * inv;
 }
 
 template <int D, bool BF16>
-hipError_t launch_gw(const DecodeArgs &a, hipStream_t stream) {
-    switch (a.heads_per_wg) {
-    case 1: return launch_typed<D, 1, BF16>(a, stream);
-    case 2: return launch_typed<D, 2, BF16>(a, stream);
-    case 4: return launch_typed<D, 4, BF16>(a, stream);
-    case 8:
-        if constexpr (D <= 128) return launch_typed<D, 8, BF16>(a, stream);
-        return hipErrorInvalidValue;
-    default: return hipErrorInvalidValue;
-    }
+hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
+    // one wave per workgroup: 32 KiB (d 128) / 64 KiB (d 256) of double-buffered tiles, so several
+    // workgroups share a CU and one's first-tile latency overlaps another's steady state
+    constexpr int NWD = 1;
+    dim3 grid((a.n_heads / a.group) * (a.group / a.heads_per_wg), a.max_splits, a.batch);
+    hipLaunchKernelGGL((decode_partial_kernel<D, NWD, BF16>), grid, dim3(64 * NWD), 0, stream, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int64_t units = (int64_t)a.batch * a.n_heads;
+    hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, a);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -254,15 +410,15 @@ hipError_t launch_gw(const DecodeArgs &a, hipStream_t stream) {
 int plan_decode(const attn_decode_params *p, DecodePlan *plan) {
     plan->head_dim = p->head_dim;
     plan->group = p->n_heads / p->n_kv_heads;
-    const int max_gw = p->head_dim <= 128 ? 8 : 4;
-    int gw = 1;
-    for (int c = 1; c <= max_gw; c *= 2)
+    int gw = 1;  // query heads per workgroup: the largest divisor of the group that fits 16 MFMA columns
+    for (int c = 1; c <= 16 && c <= plan->group; ++c)
         if (plan->group % c == 0) gw = c;
     plan->heads_per_wg = gw;
     int cap = p->max_context;
     const int64_t table_cap = (int64_t)p->max_pages_per_seq * p->page_size;
     if (table_cap < cap) cap = (int)table_cap;
-    plan->chunk = cap <= 2048 ? 128 : (cap <= 8192 ? 256 : 512);
+    // tokens per split: long enough to amortise the first tile's latency, short enough to fill the chip
+    plan->chunk = cap <= 2048 ? 128 : (cap <= 4096 ? 256 : (cap <= 8192 ? 512 : kMaxChunk));
     plan->max_splits = cap > 0 ? (cap + plan->chunk - 1) / plan->chunk : 1;
     const size_t units = (size_t)p->batch * p->n_heads;
     plan->ml_offset = 0;
@@ -306,10 +462,14 @@ hipError_t launch_paged_decode(const attn_decode_params *p, const DecodePlan *pl
     a.chunk = plan->chunk;
     a.max_splits = plan->max_splits;
     a.score_scale = p->scale * kLog2e;
+    int shift = -1;
+    for (int k = 0; k < 31; ++k)
+        if ((1 << k) == p->page_size) shift = k;
+    a.page_shift = shift;
     const bool bf16 = p->kv_dtype == ATTN_BF16;
     switch (p->head_dim) {
-    case 128: return bf16 ? launch_gw<128, true>(a, stream) : launch_gw<128, false>(a, stream);
-    case 256: return bf16 ? launch_gw<256, true>(a, stream) : launch_gw<256, false>(a, stream);
+    case 128: return bf16 ? launch_typed<128, true>(a, stream) : launch_typed<128, false>(a, stream);
+    case 256: return bf16 ? launch_typed<256, true>(a, stream) : launch_typed<256, false>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }

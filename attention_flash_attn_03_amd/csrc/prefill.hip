@@ -39,13 +39,11 @@ namespace {
 constexpr int kTile = 64;               // KV rows per step
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <int D>
-struct Geo {
-    static constexpr int CH = D / 8;         // 16-byte chunks per K/V row
-    static constexpr int KSTEPS = D / 16;    // MFMA k-steps for S
-    static constexpr int DBLK = D / 32;      // 32-column O blocks per wave
-    static constexpr int TILE_ELEMS = kTile * D;
-};
+// O and l are rescaled only when a row's running max grows by more than this
+// many binary orders of magnitude; until then the stale max stays the
+// reference, so P <= 2^8 (fine in f16, bf16 and the fp32 sums) and O / l is
+// unchanged.  Rescales then happen a few times per row instead of per tile.
+constexpr float kRescaleThreshold = 8.f;
 
 struct PrefillArgs {
     const void *q, *k, *v, *mask;
@@ -53,13 +51,19 @@ struct PrefillArgs {
     const uint8_t *blk;
     float *part;       // split partials (unnormalised O)
     float2 *ml;        // split partials (running max in log2 units, running sum)
+    float *pair_part;  // paired row blocks: unnormalised O of each side [pairs][2][slots][D]
+    float2 *pair_ml;   // paired row blocks: (m, l) of each side [pairs][2][slots]
+    uint32_t *pair_cnt;  // paired row blocks: sides finished [pairs] (zeroed by the classify pass)
     int64_t q_bs, q_rs, q_hs, k_bs, k_rs, k_hs, v_bs, v_rs, v_hs, m_bs, m_hs, m_rs, o_bs, o_rs, o_hs;
     int batch, rows, kv_len, n_heads, group;
     int rows_per_wg, heads_per_wg, row_blocks, head_groups, blk_heads;
     int kv_tiles, blk_stride, splits, tiles_per_split;
-    int q_bf16, mask_bf16, mask_vec;
+    int q_bf16, mask_bf16, mask_vec, mask_dma, pairing, n_pair_cnt;
     float score_scale;  // scale * log2(e)
 };
+
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bhalf2v __attribute__((ext_vector_type(2)));
 
 template <bool BF16>
 __device__ __forceinline__ float16v mfma32(uint4v a, uint4v b, float16v c) {
@@ -81,21 +85,30 @@ __device__ __forceinline__ uint16_t to_kv16(float x) {
     }
 }
 
+// Two probabilities rounded to the K/V type (v_cvt_pk_{f16,bf16}_f32) and
+// their exact sum as rounded (v_dot2 against (1, 1), fp32 accumulation).
 template <bool BF16>
-__device__ __forceinline__ float from_kv16(uint16_t x) {
+__device__ __forceinline__ uint32_t pack_p(float p0, float p1, float &sum) {
     if constexpr (BF16) {
-        return bf16_bits_to_f32(x);
+        const bhalf2v v = {(__bf16)p0, (__bf16)p1};
+        sum = __builtin_amdgcn_fdot2_f32_bf16(v, bhalf2v{(__bf16)1.f, (__bf16)1.f}, sum, false);
+        return __builtin_bit_cast(uint32_t, v);
     } else {
-        return f16_bits_to_f32(x);
+        const half2v v = {(_Float16)p0, (_Float16)p1};
+        sum = __builtin_amdgcn_fdot2(v, half2v{(_Float16)1.f, (_Float16)1.f}, sum, false);
+        return __builtin_bit_cast(uint32_t, v);
     }
 }
 
 typedef __attribute__((address_space(3))) short4v lds_short4;
 typedef __attribute__((address_space(3))) void lds_void;
-typedef __attribute__((address_space(1))) void global_void;
+typedef const __attribute__((address_space(4))) uint32_t const_u32;
 
-__device__ __forceinline__ short4v read_tr16(const uint16_t *lds_ptr) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(lds_ptr));
+// two consecutive ds_read_b64_tr_b16 results form one MFMA operand as read
+__device__ __forceinline__ uint4v read_tr16_pair(const uint16_t *p0, const uint16_t *p1) {
+    const uint2 lo = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)p0));
+    const uint2 hi = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)p1));
+    return uint4v{lo.x, lo.y, hi.x, hi.y};
 }
 
 // LDS tile layouts (64 rows x D, no padding).  Chunk = 16 bytes = 8 elements.
@@ -107,51 +120,111 @@ __device__ __forceinline__ short4v read_tr16(const uint16_t *lds_ptr) {
 __device__ __forceinline__ int k_swz(int row) { return row & 15; }
 __device__ __forceinline__ int v_swz(int row) { return (row & 3) << 2; }
 
-// Stream one 64-row tile of K or V into LDS with global_load_lds_dwordx4: a
+// Row strides (elements) below this keep every offset inside a 64-row stage under 2^32 bytes.
+constexpr int64_t kOff32Stride = (int64_t)1 << 25;
+
+constexpr int cgcd(int x, int y) { return y == 0 ? x : cgcd(y, x % y); }
+
+// A wave-uniform pointer, made visibly uniform so that it can live in SGPRs.
+__device__ __forceinline__ const char *uniform_ptr(const char *p) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const char *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Streams BK-row stages of K or V into LDS with global_load_lds_dwordx4: a
 // wave-instruction fills 64 consecutive 16-byte LDS slots starting at M0, so
-// each lane fetches the global chunk that belongs in its slot.  Rows past
-// kv_len fetch row kv_len-1 (finite data; those keys are masked to -inf).
-// Every wave issues exactly NLD instructions; the explicit vmcnt waits below
-// count them.  The instruction is issued from inline asm so the compiler does
-// not treat every later LDS read as dependent on it (its conservative
-// vmcnt(0) would drain the prefetch of the other tile); its own waits for
-// other loads only get stricter, never weaker, from loads it cannot see.
-template <int D, int NW, bool IS_V>
-__device__ __forceinline__ void issue_tile(uint16_t *lds, const uint16_t *base, int64_t row_stride, int key0,
-                                           int kv_len, int wave, int lane) {
-    constexpr int CH = D / 8;
-    constexpr int NLD = kTile * CH / (64 * NW);
-    // recompute the per-lane addresses here instead of keeping 2*NLD of them live across the loop
-    asm volatile("" : "+v"(lane));
-    const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void *)lds;
+// each lane fetches the global chunk that belongs in its slot.  Instruction
+// `it` of wave w covers rows row0 = (it*NW + w)*RPI .. +RPI-1; a lane's row
+// within them (lrow) is fixed and its swizzled chunk repeats with a short
+// period in `it`, so the lane offsets are computed once and each instruction
+// only needs a scalar row base (no vector arithmetic per load).  Rows past
+// kv_len (last stage only) fetch row kv_len-1: finite data whose keys are
+// masked to -inf.
+//
+// The loads are issued from inline asm so the compiler does not treat every
+// later LDS read as dependent on them (its conservative vmcnt(0) would drain
+// the prefetch of the next stage); the explicit waits in the kernel cover
+// them.  M0 is a reserved register that inline asm may not declare
+// clobbered; nothing else in these kernels reads it (no movrel, sendmsg or
+// LDS-DMA intrinsic), so writing it here is safe.
+template <int D, int NW, int BK, bool IS_V>
+struct TileStream {
+    static constexpr int CH = D / 8;
+    static constexpr int RPI = 64 / CH;                  // rows per instruction
+    static constexpr int GR = NW * RPI;                  // rows one instruction of every wave covers
+    static constexpr int NLD = BK / GR;                  // instructions per wave per stage
+    // the swizzle term of instruction `it` repeats with period P in `it`
+    static constexpr int PERIOD_ROWS = IS_V ? 4 : 16;
+    static constexpr int P = PERIOD_ROWS / cgcd(PERIOD_ROWS, GR) < NLD ? PERIOD_ROWS / cgcd(PERIOD_ROWS, GR) : NLD;
+    int lrow, inv;
+    uint32_t voff[P];   // byte offset of this lane's 16 bytes from the instruction's first row
+
+    __device__ __forceinline__ void init(int lane, int wave, int64_t row_stride) {
+        lrow = lane / CH;
+        const int lch = lane % CH;
+        inv = lch ^ (IS_V ? 4 * lrow : lrow);
 #pragma unroll
-    for (int it = 0; it < NLD; ++it) {
-        const int slot0 = (it * NW + wave) * 64;
-        const int slot = slot0 + lane;
-        const int row = slot / CH;
-        const int pch = slot % CH;
-        const int ch = pch ^ (IS_V ? v_swz(row) : k_swz(row));
-        int grow = key0 + row;
-        grow = grow < kv_len ? grow : kv_len - 1;
-        const uint16_t *src = base + (int64_t)grow * row_stride + ch * 8;
-        const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base + slot0 * 16);
-        // M0 is a reserved register the compiler does not let inline asm clobber; nothing
-        // else in this kernel reads it (no movrel, sendmsg or LDS-DMA intrinsic), so writing
-        // it here is safe.
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory");
+        for (int r = 0; r < P; ++r)
+            voff[r] = (uint32_t)((lrow * row_stride + 8 * (inv ^ uniform_swz((r * NW + wave) * RPI))) * 2);
     }
+    __device__ __forceinline__ static int uniform_swz(int row0) { return IS_V ? 4 * (row0 & 3) : (row0 & 15); }
+
+    // A stage of BK rows that all exist: one scalar base per stage and a 32-bit
+    // lane offset per instruction (the row stride times BK rows fits in 32 bits,
+    // which the caller checks).
+    __device__ __forceinline__ void issue_full(uint16_t *lds, const uint16_t *base, int64_t row_stride, int key0,
+                                               int wave) const {
+        const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void *)lds;
+        const char *stage = uniform_ptr((const char *)(base + (int64_t)(key0 + wave * RPI) * row_stride));
+        const uint32_t step = (uint32_t)(GR * row_stride * 2);
+#pragma unroll
+        for (int it = 0; it < NLD; ++it) {
+            const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base + (it * NW + wave) * 1024);
+            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff[it % P] + it * step),
+                         "s"(stage)
+                         : "memory");
+        }
+    }
+    // The ragged last stage: rows past kv_len fetch row kv_len-1 instead.
+    __device__ __forceinline__ void issue_tail(uint16_t *lds, const uint16_t *base, int64_t row_stride, int key0,
+                                               int kv_len, int wave) const {
+        const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void *)lds;
+#pragma unroll 1
+        for (int it = 0; it < NLD; ++it) {
+            const int row0 = (it * NW + wave) * RPI;
+            const int ch = inv ^ uniform_swz(row0);
+            int grow = key0 + row0 + lrow;
+            grow = grow < kv_len ? grow : kv_len - 1;
+            const uint16_t *src = base + (int64_t)grow * row_stride + ch * 8;
+            const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base + (it * NW + wave) * 1024);
+            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory");
+        }
+    }
+    __device__ __forceinline__ void issue(uint16_t *lds, const uint16_t *base, int64_t row_stride, int key0,
+                                          int kv_len, int wave, bool full) const {
+        if (full && row_stride < kOff32Stride) issue_full(lds, base, row_stride, key0, wave);
+        else issue_tail(lds, base, row_stride, key0, kv_len, wave);
+    }
+};
+
+// x *= f for an accumulator element that lives in an AGPR.  Written out so that
+// the only vector-ALU access to the O accumulator is this rare rescale: the
+// compiler then keeps the accumulator in AGPRs next to the MFMAs instead of
+// copying it to VGPRs on every stage.
+__device__ __forceinline__ float scale_acc(float x, float f) {
+    float t;
+    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
+                 : "+a"(x), "=&v"(t)
+                 : "v"(f));
+    return x;
 }
 
-// Wait until at most N of this wave's vector-memory operations are in flight,
-// then meet the other waves.  Loads retire in order, so N = the count issued
-// after the ones we need.
-template <int N>
-__device__ __forceinline__ void wait_vm_barrier() {
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
-}
+// Wait until every vector-memory operation of this wave has landed, then
+// meet the other waves.
+__device__ __forceinline__ void wait_all_barrier() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
 __device__ __forceinline__ void lds_done_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-typedef const __attribute__((address_space(4))) uint32_t const_u32;
 
 // QSPLIT: f32 Q against bf16 K/V.  bf16 keeps 8 significant bits, which
 // perturbs every score by about 2^-9 relative; Q is carried as hi + lo bf16
@@ -160,32 +233,144 @@ typedef const __attribute__((address_space(4))) uint32_t const_u32;
 // NW waves per workgroup; with head_dim 512 the waves pair up as two slices
 // of 256 head-dim columns over the same 32 query slots (NS = 2) and add their
 // partial scores through LDS; otherwise every wave has its own query slots.
+// A stage is BK keys (64, or 32 at head_dim 512 so two stages fit in LDS);
+// the tile codes cover 64 keys.
+//
+// Schedule of stage j (K/V of j are in buffer j%2, requested one stage ago):
+//   touch mask(j) registers and wait for everything -> K(j), V(j), mask(j) landed
+//   request mask(j+1) (registers) and K(j+1), V(j+1) (the other LDS buffer)
+//   S^T = K Q^T, scale + mask, online softmax, O^T += V^T P^T
+//   barrier (every wave is done with buffer j%2)
+// so each stage's loads have a whole stage of compute to land, and no wait for
+// a load the compiler can see ever drains the prefetch (loads retire in order,
+// and the mask loads are always requested before the stage they belong to).
 template <int D, int NW, bool BF16, bool HAS_MASK, bool QSPLIT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_kernel(PrefillArgs a) {
-    using G = Geo<D>;
     constexpr int NS = D > 256 ? 2 : 1;       // head-dim slices
     constexpr int DS = D / NS;                 // columns per wave
     constexpr int KSTEPS = DS / 16;            // MFMA k-steps of S over a slice
     constexpr int DBLK = DS / 32;              // 32-column O blocks per wave
-    constexpr int NLD = kTile * G::CH / (64 * NW);
-    __shared__ __attribute__((aligned(1024))) uint16_t k_lds[G::TILE_ELEMS];
-    __shared__ __attribute__((aligned(1024))) uint16_t v_lds[G::TILE_ELEMS];
-    __shared__ __attribute__((aligned(16))) float x_lds[NS > 1 ? NW * 2 * 16 * 64 : 1];
+    // keys per stage: two stages of K and V fit in LDS with room for the other resident
+    // workgroups (512 * D bytes at 64 keys), and the f32-Q split at head_dim 256 stays
+    // within the register file
+    constexpr int BK = (D > 256 || (D == 256 && (NW == 2 || QSPLIT))) ? 32 : 64;
+    constexpr int NB = BK / 32;                // 32-key blocks per stage
+    constexpr int SPT = kTile / BK;            // stages per 64-key tile code
+    constexpr int STAGE_ELEMS = BK * D;
+    using KS = TileStream<D, NW, BK, false>;
+    using VS = TileStream<D, NW, BK, true>;
+    __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2 * STAGE_ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2 * STAGE_ELEMS];
+    __shared__ __attribute__((aligned(16))) float4v x_lds[NS > 1 ? NW * NB * 4 * 64 : 1];
+    constexpr int QW = NW / NS;                // query waves
+    constexpr int MI = 2 * NB;                 // mask DMA instructions per query wave per stage
+    __shared__ __attribute__((aligned(1024))) uint4v m_lds[HAS_MASK ? 2 * QW * MI * 64 : 1];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int slice = wave % NS;
     const int qwave = wave / NS;
     const int half = lane >> 5;    // which 8-element k half of an MFMA operand this lane feeds
     const int col = lane & 31;     // query slot column inside the wave
 
-    // longest-first: with a causal frontier the last row blocks carry the most tiles
-    const int rb = a.row_blocks - 1 - (int)blockIdx.x;
-    const int hg = blockIdx.y;
-    const int b = blockIdx.z / a.splits;
-    const int split = blockIdx.z % a.splits;
+    // 1-D grid: head group fastest (consecutive workgroups go to consecutive XCDs, so the
+    // workgroups of one KV head share an L2), then row blocks, then split and batch.
+    int lin = blockIdx.x;
+    const int hg = lin % a.head_groups;
+    lin /= a.head_groups;
+    const int idx = lin % a.row_blocks;
+    lin /= a.row_blocks;
+    const int split = lin % a.splits;
+    const int b = lin / a.splits;
     const int h0 = hg * a.heads_per_wg;
     const int kvh = h0 / a.group;
+    const int n_stages = (a.kv_len + BK - 1) / BK;
+    const int split_begin = split * a.tiles_per_split * SPT;
+    const int split_end = min(split_begin + a.tiles_per_split * SPT, n_stages);
+
+    // tile codes are read as dwords through the scalar cache (constant address space)
+    auto code_row = [&](int rbx) -> const_u32 * {
+        const int bh = a.blk_heads == 1 ? 0 : hg;
+        return (const_u32 *)(a.blk + (((int64_t)b * a.blk_heads + bh) * a.row_blocks + rbx) * a.blk_stride);
+    };
+    // stages of a row block that are not skipped, and the stage after the first `cut` of them
+    auto count_stages = [&](const_u32 *row) {
+        int n = 0;
+        for (int w = 0; w < a.blk_stride / 4; ++w) {
+            const uint32_t word = row[w];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = 4 * w + j;
+                if (t < a.kv_tiles && ((word >> (8 * j)) & 0xffu) != TILE_SKIP) n += min(SPT, n_stages - t * SPT);
+            }
+        }
+        return n;
+    };
+    auto stage_after = [&](const_u32 *row, int cut) {
+        int n = 0;
+        for (int w = 0; w < a.blk_stride / 4; ++w) {
+            const uint32_t word = row[w];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = 4 * w + j;
+                if (t < a.kv_tiles && ((word >> (8 * j)) & 0xffu) != TILE_SKIP) {
+                    const int k = min(SPT, n_stages - t * SPT);
+                    if (n + k >= cut) return t * SPT + (cut - n);
+                    n += k;
+                }
+            }
+        }
+        return n_stages;
+    };
+
+    // The tasks of this workgroup: a row block and a stage range each.  Without
+    // pairing it is one row block (the last ones first: a causal frontier makes them
+    // the heaviest).  With pairing, row blocks lo = p and hi = RB-1-p share two
+    // workgroups: side 0 takes the first half of their unskipped stages from hi,
+    // side 1 the rest of hi and then all of lo, so both sides carry the same load
+    // whatever the mask; when hi is cut, the side that finishes it second merges the
+    // two partial results.
+    int rb0 = a.row_blocks - 1 - idx, beg0 = split_begin, end0 = split_end, side0 = -1;
+    int rb1 = 0, beg1 = 0, end1 = 0, ntask = 1, pair = 0;
+    if constexpr (HAS_MASK) {
+        if (a.pairing) {
+            const int npairs = a.row_blocks >> 1;
+            if (idx < 2 * npairs) {
+                pair = idx >> 1;
+                const int side = idx & 1;
+                const int rb_lo = pair, rb_hi = a.row_blocks - 1 - pair;
+                const int w_hi = count_stages(code_row(rb_hi));
+                const int w_lo = count_stages(code_row(rb_lo));
+                const int cut = min((w_hi + w_lo + 1) >> 1, w_hi);
+                const bool shared = cut > 0 && cut < w_hi;
+                const int s_cut = shared ? stage_after(code_row(rb_hi), cut) : n_stages;
+                beg0 = 0;
+                end0 = n_stages;
+                if (side == 0) {
+                    rb0 = rb_hi;
+                    end0 = s_cut;
+                    side0 = shared ? 0 : -1;
+                } else if (shared) {
+                    rb0 = rb_hi;
+                    beg0 = s_cut;
+                    side0 = 1;
+                    rb1 = rb_lo;
+                    end1 = n_stages;
+                    ntask = 2;
+                } else {
+                    rb0 = rb_lo;
+                }
+            } else {
+                rb0 = npairs;  // the middle row block of an odd count
+            }
+        }
+    }
+
+    for (int task = 0; task < ntask; ++task) {
+    const int rb = task == 0 ? rb0 : rb1;
+    const int st_begin = task == 0 ? beg0 : beg1;
+    const int st_end = task == 0 ? end0 : end1;
+    const int side = task == 0 ? side0 : -1;
 
     // this lane's query slot
     const int slot = qwave * 32 + col;
@@ -262,31 +447,73 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     for (int db = 0; db < DBLK; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.f;
-    float m_run = -INFINITY;  // running max of the log2-scaled scores
+    float m_run = -INFINITY;  // reference max of the log2-scaled scores (at most kRescaleThreshold stale)
     float l_run = 0.f;        // running sum of the rounded probabilities
 
     const uint16_t *kbase = (const uint16_t *)a.k + b * a.k_bs + kvh * a.k_hs;
     const uint16_t *vbase = (const uint16_t *)a.v + b * a.v_bs + kvh * a.v_hs;
-    // tile codes are read as dwords through the scalar cache (constant address space)
     const_u32 *blk_row = nullptr;
-    if constexpr (HAS_MASK) {
-        const int bh = a.blk_heads == 1 ? 0 : hg;
-        blk_row = (const_u32 *)(a.blk + (((int64_t)b * a.blk_heads + bh) * a.row_blocks + rb) * a.blk_stride);
-    }
-    auto tile_code = [&](int t) -> int {
+    if constexpr (HAS_MASK) blk_row = code_row(rb);
+    auto stage_code = [&](int st) -> int {
         if constexpr (HAS_MASK) {
+            const int t = st / SPT;
             return (int)((blk_row[t >> 2] >> (8 * (t & 3))) & 0xffu);
         } else {
             return TILE_OPEN;
         }
     };
-    const int kt_begin = split * a.tiles_per_split;
-    const int kt_end = min(kt_begin + a.tiles_per_split, a.kv_tiles);
-    auto next_tile = [&](int from) {
-        int t = from;
-        while (t < kt_end && tile_code(t) == TILE_SKIP) ++t;
-        return t < kt_end ? t : kt_end;
+    auto next_stage = [&](int from) {
+        int st = from;
+        while (st < st_end && stage_code(st) == TILE_SKIP) ++st;
+        return st < st_end ? st : st_end;
     };
+    // Mask of a stage.  Full stages of a 16-byte aligned mask are streamed into LDS
+    // beside K and V: instruction i of a query wave fetches, for each of its 32 query
+    // rows, the 8-key chunks 2i (lanes 0..31) and 2i+1 (lanes 32..63), so that all 64
+    // lanes reading one chunk touch 512 contiguous bytes.  Other stages (the ragged
+    // last one, or a mask of other alignment) are read from memory where they are used.
+    auto mask_in_lds = [&](int st) { return a.mask_dma && st * BK + BK <= a.kv_len; };
+    auto issue_mask = [&](int st, int bufi) {
+        const uint32_t mbase = (uint32_t)(uintptr_t)(lds_void *)(m_lds + (bufi * QW + qwave) * MI * 64);
+        const uint16_t *src = mrow + st * BK + 8 * half;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            const uint32_t m0 = __builtin_amdgcn_readfirstlane(mbase + i * 1024);
+            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src + 16 * i) : "memory");
+        }
+    };
+    // raw mask values of this lane's keys in stage st: key0 + 32*bb + 8*q4 + 4*half + e
+    auto load_mask = [&](uint2 (&mr)[NB][4], int st, int bufi) {
+        const int key0 = st * BK;
+        if (mask_in_lds(st)) {
+            const uint4v *mb = m_lds + (bufi * QW + qwave) * MI * 64;
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int c = 4 * bb + q4;
+                    mr[bb][q4] = *reinterpret_cast<const uint2 *>(
+                        reinterpret_cast<const char *>(mb + (c >> 1) * 64 + (c & 1) * 32 + col) + 8 * half);
+                }
+        } else {
+            // any alignment, any tail: element loads from clamped (in-bounds) keys
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int kf = key0 + 32 * bb + 8 * q4 + 4 * half;
+                    uint16_t m16[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) m16[e] = mrow[min(kf + e, a.kv_len - 1)];
+                    mr[bb][q4] = make_uint2(pack2(m16[0], m16[1]), pack2(m16[2], m16[3]));
+                }
+        }
+    };
+
+    KS kstream;
+    VS vstream;
+    kstream.init(lane, wave, a.k_rs);
+    vstream.init(lane, wave, a.v_rs);
 
     // per-lane pieces of the transposing V read: row kb + j/4, logical chunk
     // 4*db + 2*(g&1) + (j&3)/2 (plus the slice), element 4*(j&1) inside the chunk
@@ -295,179 +522,201 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     const int v_lchunk0 = slice * (DS / 8) + 2 * (g16 & 1) + ((j16 & 3) >> 1);
     const int v_inner = 4 * (j16 & 1);
 
-    int kt = next_tile(kt_begin);
-    if (kt < kt_end) {
-        issue_tile<D, NW, false>(k_lds, kbase, a.k_rs, kt * kTile, a.kv_len, wave, lane);
-        issue_tile<D, NW, true>(v_lds, vbase, a.v_rs, kt * kTile, a.kv_len, wave, lane);
+    int st = next_stage(st_begin);
+    int buf = 0;
+    if (st < st_end) {
+        if (HAS_MASK && slice == 0 && stage_code(st) == TILE_MASKED && mask_in_lds(st)) issue_mask(st, 0);
+        const bool full = st * BK + BK <= a.kv_len;
+        kstream.issue(k_lds, kbase, a.k_rs, st * BK, a.kv_len, wave, full);
+        vstream.issue(v_lds, vbase, a.v_rs, st * BK, a.kv_len, wave, full);
     }
-    while (kt < kt_end) {
-        const int code = tile_code(kt);
-        const int nxt = next_tile(kt + 1);
-        const int key0 = kt * kTile;
-        const bool full_tile = key0 + kTile <= a.kv_len;
-
-        wait_vm_barrier<NLD>();  // K(kt) is in LDS for every wave; V(kt) may still be landing
-
-        // raw mask values of this lane's 32 keys (key0 + 32*blk2 + 8*q4 + 4*half + e); with two
-        // slices only slice 0 adds the mask into its partial scores
-        uint2 mraw[2][4];
+    while (st < st_end) {
+        const int code = stage_code(st);
+        const int nxt = next_stage(st + 1);
+        const int key0 = st * BK;
+        const bool full_stage = key0 + BK <= a.kv_len;
         const bool use_mask = HAS_MASK && code == TILE_MASKED && slice == 0;
-        if constexpr (HAS_MASK) {
-            if (use_mask) {
-                if (a.mask_vec && full_tile) {
-#pragma unroll
-                    for (int blk2 = 0; blk2 < 2; ++blk2)
-#pragma unroll
-                        for (int q4 = 0; q4 < 4; ++q4)
-                            mraw[blk2][q4] = *reinterpret_cast<const uint2 *>(mrow + key0 + 32 * blk2 + 8 * q4 + 4 * half);
-                } else {
-                    // any alignment, any tail: element loads from clamped (in-bounds) keys
-#pragma unroll
-                    for (int blk2 = 0; blk2 < 2; ++blk2)
-#pragma unroll
-                        for (int q4 = 0; q4 < 4; ++q4) {
-                            const int kf = key0 + 32 * blk2 + 8 * q4 + 4 * half;
-                            uint16_t m16[4];
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) m16[e] = mrow[min(kf + e, a.kv_len - 1)];
-                            mraw[blk2][q4] = make_uint2(pack2(m16[0], m16[1]), pack2(m16[2], m16[3]));
-                        }
-                }
-            }
-        }
 
-        // ---- S^T (64 keys x 32 queries) over this wave's head-dim slice
-        float16v s[2];
+        wait_all_barrier();  // K, V and mask of this stage landed (all requested one stage ago)
+
+        // request stage nxt into the other buffers
+        if (nxt < st_end) {
+            if (HAS_MASK && slice == 0 && stage_code(nxt) == TILE_MASKED && mask_in_lds(nxt)) issue_mask(nxt, buf ^ 1);
+            const bool nfull = nxt * BK + BK <= a.kv_len;
+            kstream.issue(k_lds + (buf ^ 1) * STAGE_ELEMS, kbase, a.k_rs, nxt * BK, a.kv_len, wave, nfull);
+            vstream.issue(v_lds + (buf ^ 1) * STAGE_ELEMS, vbase, a.v_rs, nxt * BK, a.kv_len, wave, nfull);
+        }
+        const uint16_t *kt_lds = k_lds + buf * STAGE_ELEMS;
+        const uint16_t *vt_lds = v_lds + buf * STAGE_ELEMS;
+
+        // ---- S^T (BK keys x 32 queries) over this wave's head-dim slice
+        float16v s[NB];
 #pragma unroll
-        for (int blk2 = 0; blk2 < 2; ++blk2) {
+        for (int bb = 0; bb < NB; ++bb) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) s[blk2][r] = 0.f;
-            const int krow = blk2 * 32 + col;
-            const uint16_t *kr = &k_lds[krow * D];
+            for (int r = 0; r < 16; ++r) s[bb][r] = 0.f;
+            const int krow = bb * 32 + col;
+            const uint16_t *kr = kt_lds + krow * D;
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks) {
                 const int lch = slice * (DS / 8) + 2 * ks + half;
                 const uint4v kf = *reinterpret_cast<const uint4v *>(kr + 8 * (lch ^ k_swz(krow)));
-                s[blk2] = mfma32<BF16>(kf, qf[ks], s[blk2]);
-                if constexpr (QSPLIT) s[blk2] = mfma32<BF16>(kf, qlo[ks], s[blk2]);
+                s[bb] = mfma32<BF16>(kf, qf[ks], s[bb]);
+                if constexpr (QSPLIT) s[bb] = mfma32<BF16>(kf, qlo[ks], s[bb]);
             }
         }
 
-        // ---- scale and mask (consumed before the next K tile is requested, so waiting for the
-        // mask loads never waits on that prefetch); this lane holds keys key0 + 32*blk2 + 8*(r/4) + 4*half + r%4
+        // ---- scale and mask; this lane holds keys key0 + 32*bb + 8*(r/4) + 4*half + r%4
+        if (use_mask) {
+            uint2 mcur[NB][4];
+            load_mask(mcur, st, buf);
 #pragma unroll
-        for (int blk2 = 0; blk2 < 2; ++blk2)
+            for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4)
+                for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float mvf = 0.f;
-                    if (use_mask) {
-                        const uint32_t word = e < 2 ? mraw[blk2][q4].x : mraw[blk2][q4].y;
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t word = e < 2 ? mcur[bb][q4].x : mcur[bb][q4].y;
                         const uint16_t m16 = (uint16_t)(word >> (16 * (e & 1)));
-                        mvf = (a.mask_bf16 ? bf16_bits_to_f32(m16) : f16_bits_to_f32(m16)) * kLog2e;
+                        const float mvf = (a.mask_bf16 ? bf16_bits_to_f32(m16) : f16_bits_to_f32(m16)) * kLog2e;
+                        s[bb][4 * q4 + e] = fmaf(s[bb][4 * q4 + e], a.score_scale, mvf);
                     }
-                    s[blk2][4 * q4 + e] = fmaf(s[blk2][4 * q4 + e], a.score_scale, mvf);
-                }
-        if constexpr (NS > 1) {
+        } else {
 #pragma unroll
-            for (int blk2 = 0; blk2 < 2; ++blk2)
+            for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) x_lds[((wave * 2 + blk2) * 16 + r) * 64 + lane] = s[blk2][r];
+                for (int r = 0; r < 16; ++r) s[bb][r] *= a.score_scale;
         }
-        lds_done_barrier();  // every wave is done with K(kt) (and has posted its partial scores)
-        if (nxt < kt_end) issue_tile<D, NW, false>(k_lds, kbase, a.k_rs, nxt * kTile, a.kv_len, wave, lane);
         if constexpr (NS > 1) {
+            // add the other slice's partial scores
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4)
+                    x_lds[((wave * NB + bb) * 4 + r4) * 64 + lane] =
+                        float4v{s[bb][4 * r4], s[bb][4 * r4 + 1], s[bb][4 * r4 + 2], s[bb][4 * r4 + 3]};
+            lds_done_barrier();
             const int other = qwave * NS + (1 - slice);
 #pragma unroll
-            for (int blk2 = 0; blk2 < 2; ++blk2)
+            for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s[blk2][r] += x_lds[((other * 2 + blk2) * 16 + r) * 64 + lane];
+                for (int r4 = 0; r4 < 4; ++r4) {
+                    const float4v x = x_lds[((other * NB + bb) * 4 + r4) * 64 + lane];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s[bb][4 * r4 + e] += x[e];
+                }
         }
-        if (!full_tile) {
+        if (!full_stage) {
 #pragma unroll
-            for (int blk2 = 0; blk2 < 2; ++blk2)
+            for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    if (key0 + 32 * blk2 + 8 * (r >> 2) + 4 * half + (r & 3) >= a.kv_len) s[blk2][r] = -INFINITY;
+                    if (key0 + 32 * bb + 8 * (r >> 2) + 4 * half + (r & 3) >= a.kv_len) s[bb][r] = -INFINITY;
         }
 
-        // ---- online softmax for this lane's query (32 keys here, 32 in lane ^ 32)
+        // ---- online softmax for this lane's query (BK/2 keys here, BK/2 in lane ^ 32)
         float mx = -INFINITY;
 #pragma unroll
-        for (int blk2 = 0; blk2 < 2; ++blk2)
+        for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[blk2][r]);
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[bb][r]);
         mx = max_with_other_half(mx);
-        const float m_new = fmaxf(m_run, mx);
+        const bool grow = mx > m_run + kRescaleThreshold;  // also true for the first visible key
+        const float m_new = grow ? mx : m_run;
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_use);
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
         float rowsum = 0.f;
-        uint4v pb[4];  // B operands of O^T += V^T P^T: pb[2*blk2 + e] holds regs 8e..8e+7 of s[blk2]
+        uint4v pb[2 * NB];  // B operands of O^T += V^T P^T: pb[2*bb + e] holds regs 8e..8e+7 of s[bb]
 #pragma unroll
-        for (int blk2 = 0; blk2 < 2; ++blk2) {
+        for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                uint16_t p16[8];
+                uint32_t w[4];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    p16[i] = to_kv16<BF16>(exp2f(s[blk2][8 * e + i] - m_use));
-                    rowsum += from_kv16<BF16>(p16[i]);
-                }
-                pb[2 * blk2 + e] = uint4v{pack2(p16[0], p16[1]), pack2(p16[2], p16[3]), pack2(p16[4], p16[5]),
-                                          pack2(p16[6], p16[7])};
+                for (int i = 0; i < 4; ++i)
+                    w[i] = pack_p<BF16>(__builtin_amdgcn_exp2f(s[bb][8 * e + 2 * i] - m_use),
+                                        __builtin_amdgcn_exp2f(s[bb][8 * e + 2 * i + 1] - m_use), rowsum);
+                pb[2 * bb + e] = uint4v{w[0], w[1], w[2], w[3]};
             }
-        }
         rowsum = sum_with_other_half(rowsum);
         l_run = l_run * alpha + rowsum;
         m_run = m_new;
-        if (__ballot(alpha != 1.f)) {
+        if (__ballot(grow)) {
 #pragma unroll
             for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc_o[db][r] *= alpha;
-        }
-
-        // V(kt) landed for every wave (K(nxt) may still be in flight)
-        if (nxt < kt_end) {
-            wait_vm_barrier<NLD>();
-        } else {
-            wait_vm_barrier<0>();
+                for (int r = 0; r < 16; ++r) acc_o[db][r] = scale_acc(acc_o[db][r], alpha);
         }
 
         // ---- O^T[d][query] += V^T[d][key] P^T[key][query]
-        // A operand slot i of lane (m, half) is key 32*blk2 + 16*e + 8*(i/4) + 4*half + i%4, column m.
+        // A operand slot i of lane (m, half) is key 32*bb + 16*e + 8*(i/4) + 4*half + i%4, column m.
         // A 16-lane group g reads 4 keys x 16 columns per ds_read_b64_tr_b16: lane j of the
         // group points at row kb + j/4, columns c0 + 4*(j%4) .. +3; lane j receives
         // rows kb..kb+3 of column c0 + j.
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int blk2 = u >> 1, e = u & 1;
-            const int r0 = 32 * blk2 + 16 * e + v_rsub;      // rows r0 (slots 0..3) and r0 + 8 (slots 4..7)
-            const uint16_t *vr0 = &v_lds[r0 * D + v_inner];
-            const uint16_t *vr1 = &v_lds[(r0 + 8) * D + v_inner];
+        for (int u = 0; u < 2 * NB; ++u) {
+            const int bb = u >> 1, e = u & 1;
+            const int r0 = 32 * bb + 16 * e + v_rsub;      // rows r0 (slots 0..3) and r0 + 8 (slots 4..7)
+            const uint16_t *vr0 = vt_lds + r0 * D + v_inner;
+            const uint16_t *vr1 = vt_lds + (r0 + 8) * D + v_inner;
             const int sw0 = v_swz(r0), sw1 = v_swz(r0 + 8);
 #pragma unroll
             for (int db = 0; db < DBLK; ++db) {
                 const int lch = 4 * db + v_lchunk0;
-                const short4v lo = read_tr16(vr0 + 8 * (lch ^ sw0));
-                const short4v hi = read_tr16(vr1 + 8 * (lch ^ sw1));
-                uint4v vf;
-                vf[0] = pack2((uint16_t)lo[0], (uint16_t)lo[1]);
-                vf[1] = pack2((uint16_t)lo[2], (uint16_t)lo[3]);
-                vf[2] = pack2((uint16_t)hi[0], (uint16_t)hi[1]);
-                vf[3] = pack2((uint16_t)hi[2], (uint16_t)hi[3]);
+                const uint4v vf = read_tr16_pair(vr0 + 8 * (lch ^ sw0), vr1 + 8 * (lch ^ sw1));
                 acc_o[db] = mfma32<BF16>(vf, pb[u], acc_o[db]);
             }
         }
-        lds_done_barrier();  // every wave is done with V(kt)
-        if (nxt < kt_end) issue_tile<D, NW, true>(v_lds, vbase, a.v_rs, nxt * kTile, a.kv_len, wave, lane);
-        kt = nxt;
+        lds_done_barrier();  // every wave is done with this stage's buffers
+        buf ^= 1;
+        st = nxt;
     }
 
     // ---- epilogue: this lane holds O^T columns query `col`, rows d = slice*DS + 32*db + 8*(r/4) + 4*half + r%4
-    if (!row_ok) return;
-    if (a.splits == 1) {
+    bool write_final = a.splits == 1;
+    if constexpr (HAS_MASK) {
+        if (side >= 0) {
+            // one side of a cut row block: publish this side, and if the other side is
+            // already done, merge both
+            // the arrival order is broadcast through the second mask buffer: the next task
+            // writes it only after the barrier that starts its first stage
+            int *arrival = reinterpret_cast<int *>(m_lds + QW * MI * 64);
+            const int slots = a.rows_per_wg * a.heads_per_wg;
+            const int64_t pu = ((int64_t)b * a.head_groups + hg) * (a.row_blocks >> 1) + pair;
+            float *mine = a.pair_part + ((pu * 2 + side) * slots + slot) * D + slice * DS + 4 * half;
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; ++r4)
+                    *reinterpret_cast<float4v *>(mine + 32 * db + 8 * r4) =
+                        float4v{acc_o[db][4 * r4], acc_o[db][4 * r4 + 1], acc_o[db][4 * r4 + 2], acc_o[db][4 * r4 + 3]};
+            if (slice == 0 && half == 0) a.pair_ml[(pu * 2 + side) * slots + slot] = make_float2(m_run, l_run);
+            __threadfence();
+            __syncthreads();
+            if (threadIdx.x == 0) *arrival = (int)atomicAdd(a.pair_cnt + pu, 1u);
+            __syncthreads();
+            write_final = *arrival == 1;
+            if (write_final) {
+                __threadfence();
+                const int other = 1 - side;
+                const float2 mlo = a.pair_ml[(pu * 2 + other) * slots + slot];
+                const float mx = fmaxf(m_run, mlo.x);
+                const float wa = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
+                const float wb = mlo.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mlo.x - mx);
+                const float *theirs = a.pair_part + ((pu * 2 + other) * slots + slot) * D + slice * DS + 4 * half;
+#pragma unroll
+                for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        const float4v x = *reinterpret_cast<const float4v *>(theirs + 32 * db + 8 * r4);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) acc_o[db][4 * r4 + e] = acc_o[db][4 * r4 + e] * wa + x[e] * wb;
+                    }
+                l_run = wa * l_run + wb * mlo.y;
+            }
+        }
+    }
+    if (write_final && row_ok) {
         const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
         float *orow = a.o + b * a.o_bs + (int64_t)row * a.o_rs + head * a.o_hs + slice * DS + 4 * half;
 #pragma unroll
@@ -479,7 +728,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
                 for (int e = 0; e < 4; ++e) x[e] = acc_o[db][4 * r4 + e] * inv;
                 *reinterpret_cast<float4v *>(orow + 32 * db + 8 * r4) = x;
             }
-    } else {
+    } else if (a.splits > 1 && row_ok) {
         const int64_t unit = (((int64_t)split * a.batch + b) * a.n_heads + head) * a.rows + row;
         float *prow = a.part + unit * D + slice * DS + 4 * half;
 #pragma unroll
@@ -493,13 +742,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
             }
         if (slice == 0 && half == 0) a.ml[unit] = make_float2(m_run, l_run);
     }
+    }  // task
 }
 
 // One wave classifies one (query block, 64-key tile): TILE_SKIP when every
-// entry is -inf, TILE_OPEN when every entry is zero, else TILE_MASKED.  Only
+// entry is -inf, TILE_OPEN when every entry is zero, else TILE_MASKED.  The
+// pass also clears the pair counters the attention pass uses.  Only
 // entries of real rows (< rows) and keys (< kv_len) are read.  Grid:
 // (ceil(kv_tiles / 4), row_blocks, batch * blk_heads), four waves per block.
 __global__ __launch_bounds__(256) void classify_kernel(PrefillArgs a, uint8_t *blk) {
+    if (a.n_pair_cnt > 0) {
+        // the pair counters of the attention pass start from zero on every call
+        const int64_t nthreads = (int64_t)gridDim.x * gridDim.y * gridDim.z * 256;
+        const int64_t tid = (((int64_t)blockIdx.z * gridDim.y + blockIdx.y) * gridDim.x + blockIdx.x) * 256 + threadIdx.x;
+        for (int64_t i = tid; i < a.n_pair_cnt; i += nthreads) a.pair_cnt[i] = 0u;
+    }
     const int lane = threadIdx.x & 63;
     const int kt = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (kt >= a.kv_tiles) return;
@@ -593,7 +850,7 @@ __global__ __launch_bounds__(256) void combine_kernel(PrefillArgs a) {
 
 template <int D, int NW, bool BF16, bool HAS_MASK>
 hipError_t launch_nw(const PrefillArgs &a, const PrefillPlan *plan, hipStream_t stream) {
-    dim3 grid(plan->row_blocks, plan->head_groups, (unsigned)(a.batch * plan->splits));
+    const dim3 grid((unsigned)((int64_t)plan->head_groups * plan->row_blocks * a.splits * a.batch));
     if constexpr (BF16) {
         if (!a.q_bf16) {
             hipLaunchKernelGGL((prefill_kernel<D, NW, true, HAS_MASK, true>), grid, dim3(64 * NW), 0, stream, a);
@@ -658,6 +915,14 @@ int plan_prefill(const attn_prefill_params *p, PrefillPlan *plan) {
         if (g % d == 0 && rpw * d <= max_slots) hpw = d;
     while ((rpw * hpw) % 64 != 0) rpw *= 2;
     while (rpw * hpw < max_slots && rpw < p->rows) rpw *= 2;
+    // fewer, larger workgroups reuse each K/V tile more; below two workgroups per CU
+    // (one wave per SIMD each) an unpaired causal tail dominates, so halve them
+    // (masked calls pair heavy and light row blocks instead)
+    if (plan->slices == 1 && rpw * hpw == 128 && p->mask_dtype == ATTN_NONE &&
+        (int64_t)p->batch * (p->n_heads / hpw) * ((p->rows + rpw - 1) / rpw) < 512) {
+        if (rpw >= 64) rpw /= 2;
+        else if (hpw >= 2) hpw /= 2;
+    }
     plan->rows_per_wg = rpw;
     plan->heads_per_wg = hpw;
     plan->query_waves = rpw * hpw / 32;
@@ -697,6 +962,25 @@ int plan_prefill(const attn_prefill_params *p, PrefillPlan *plan) {
     } else {
         plan->ml_offset = plan->ml_bytes = plan->part_offset = plan->part_bytes = 0;
     }
+    // paired row blocks (masked calls without a KV split): one partial result per side
+    // of every pair, and a counter per pair
+    plan->pairing = p->mask_dtype != ATTN_NONE && plan->splits == 1 && plan->row_blocks >= 2;
+    if (plan->pairing) {
+        const size_t pairs = (size_t)p->batch * plan->head_groups * (plan->row_blocks / 2);
+        const size_t slots = (size_t)plan->rows_per_wg * plan->heads_per_wg;
+        plan->pair_cnt_offset = off;
+        plan->pair_cnt_bytes = pairs * sizeof(uint32_t);
+        off = align256(off + plan->pair_cnt_bytes);
+        plan->pair_ml_offset = off;
+        plan->pair_ml_bytes = pairs * 2 * slots * sizeof(float2);
+        off = align256(off + plan->pair_ml_bytes);
+        plan->pair_part_offset = off;
+        plan->pair_part_bytes = pairs * 2 * slots * D * sizeof(float);
+        off = align256(off + plan->pair_part_bytes);
+    } else {
+        plan->pair_cnt_offset = plan->pair_cnt_bytes = plan->pair_ml_offset = plan->pair_ml_bytes = 0;
+        plan->pair_part_offset = plan->pair_part_bytes = 0;
+    }
     plan->workspace_bytes = off;
     return ATTN_OK;
 }
@@ -713,6 +997,11 @@ hipError_t launch_prefill(const attn_prefill_params *p, const PrefillPlan *plan,
     a.blk = plan->blk_bytes ? w + plan->blk_offset : nullptr;
     a.ml = plan->splits > 1 ? (float2 *)(w + plan->ml_offset) : nullptr;
     a.part = plan->splits > 1 ? (float *)(w + plan->part_offset) : nullptr;
+    a.pairing = plan->pairing;
+    a.pair_cnt = plan->pairing ? (uint32_t *)(w + plan->pair_cnt_offset) : nullptr;
+    a.pair_ml = plan->pairing ? (float2 *)(w + plan->pair_ml_offset) : nullptr;
+    a.pair_part = plan->pairing ? (float *)(w + plan->pair_part_offset) : nullptr;
+    a.n_pair_cnt = plan->pairing ? (int)(plan->pair_cnt_bytes / sizeof(uint32_t)) : 0;
     a.q_bs = p->q_bs; a.q_rs = p->q_rs; a.q_hs = p->q_hs;
     a.k_bs = p->k_bs; a.k_rs = p->k_rs; a.k_hs = p->k_hs;
     a.v_bs = p->v_bs; a.v_rs = p->v_rs; a.v_hs = p->v_hs;
@@ -737,6 +1026,9 @@ hipError_t launch_prefill(const attn_prefill_params *p, const PrefillPlan *plan,
     // 8-byte mask loads need every row start 8-byte aligned
     a.mask_vec = a.mask && (p->m_rs % 4 == 0) && (p->m_hs % 4 == 0) && (p->m_bs % 4 == 0) &&
                  (((uintptr_t)mask & 7u) == 0);
+    // 16-byte mask chunks streamed into LDS need every row start 16-byte aligned
+    a.mask_dma = a.mask && (p->m_rs % 8 == 0) && (p->m_hs % 8 == 0) && (p->m_bs % 8 == 0) &&
+                 (((uintptr_t)mask & 15u) == 0);
     a.score_scale = p->scale * kLog2e;
 
     if (a.mask) {

@@ -76,62 +76,68 @@ def main():
         return t.to(dev)
 
     print("bench: building inputs", file=sys.stderr, flush=True)
+    want = {"prefill", "decode", "verify"} if args.rows_only is None else {args.rows_only}
     # ---------------- prefill (causal, 2048 x 2048)
     pc = workloads.prefill_case("causal2k")
-    pq, pk, pv, pm = to_dev(pc.q), to_dev(pc.k), to_dev(pc.v), to_dev(pc.mask)
-    po = torch.empty(pc.q.shape, dtype=torch.float32, device=dev)
-    pp = fa.prefill_params(pq, pk, pv, pm, po, scale=pc.scale)
-    pws = torch.empty(max(1, fa.prefill_workspace_bytes(pp)), dtype=torch.uint8, device=dev)
     m = pc.meta
     prefill_flops = 4.0 * m["n_heads"] * m["head_dim"] * pc.visible_pairs
+    if "prefill" in want:
+        pq, pk, pv, pm = to_dev(pc.q), to_dev(pc.k), to_dev(pc.v), to_dev(pc.mask)
+        po = torch.empty(pc.q.shape, dtype=torch.float32, device=dev)
+        pp = fa.prefill_params(pq, pk, pv, pm, po, scale=pc.scale)
+        pws = torch.empty(max(1, fa.prefill_workspace_bytes(pp)), dtype=torch.uint8, device=dev)
 
     # ---------------- paged decode
-    dc = workloads.paged_case()
-    dq = to_dev(dc.q)
-    dkp, dvp = to_dev(dc.k_pool), to_dev(dc.v_pool)
-    dpt, dctx = to_dev(dc.page_table), to_dev(dc.context_lens)
-    do = torch.empty(dc.q.shape, dtype=torch.float32, device=dev)
-    dp = fa.decode_params(dq, dkp, dvp, dpt, do, scale=dc.scale, max_context=dc.max_context)
-    dws = torch.empty(fa.decode_workspace_bytes(dp), dtype=torch.uint8, device=dev)
-    dm = dc.meta
-    ctx = dc.context_lens.astype(np.int64)
-    decode_bytes = (float(ctx.sum()) * dm["n_kv_heads"] * dm["head_dim"] * 2 * 2      # K and V rows, f16
-                    + dc.q.nbytes + dc.q.nbytes                                       # Q in, O out (f32)
-                    + 4.0 * float(np.sum(-(-ctx // dm["page_size"])))                 # page-table entries
-                    + 4.0 * dm["batch"])                                              # context lengths
-    decode_flops = 4.0 * dm["n_heads"] * dm["head_dim"] * float(ctx.sum())
+    dm = dict(batch=64, page_size=16, num_pages=65536, n_heads=32, n_kv_heads=8, head_dim=128)
+    if "decode" in want:
+        dc = workloads.paged_case()
+        dq = to_dev(dc.q)
+        dkp, dvp = to_dev(dc.k_pool), to_dev(dc.v_pool)
+        dpt, dctx = to_dev(dc.page_table), to_dev(dc.context_lens)
+        do = torch.empty(dc.q.shape, dtype=torch.float32, device=dev)
+        dp = fa.decode_params(dq, dkp, dvp, dpt, do, scale=dc.scale, max_context=dc.max_context)
+        dws = torch.empty(fa.decode_workspace_bytes(dp), dtype=torch.uint8, device=dev)
+        dm = dc.meta
+        ctx = dc.context_lens.astype(np.int64)
+        decode_bytes = (float(ctx.sum()) * dm["n_kv_heads"] * dm["head_dim"] * 2 * 2      # K and V rows, f16
+                        + dc.q.nbytes + dc.q.nbytes                                       # Q in, O out (f32)
+                        + 4.0 * float(np.sum(-(-ctx // dm["page_size"])))                 # page-table entries
+                        + 4.0 * dm["batch"])                                              # context lengths
+        decode_flops = 4.0 * dm["n_heads"] * dm["head_dim"] * float(ctx.sum())
 
     # ---------------- block verify
-    vc = workloads.dflash_case()
-    b, h, hk, d, r, w = vc.geom
+    vc = workloads.dflash_case() if "verify" in want else None
+    b, h, hk, d, r, w = (4, 32, 8, 128, 16, 4096) if vc is None else vc.geom
     klen = w - 1 + r
-    vp = fa.DFlashParams(b, h, hk, d, r, w, klen, vc.max_commit)
-    ring_k, ring_v = to_dev(vc.ring_k, True), to_dev(vc.ring_v, True)
-    cq, ck, cv = to_dev(vc.cur_q), to_dev(vc.cur_k), to_dev(vc.cur_v)
-    vL, vwp, vcnt = to_dev(vc.cache_lengths), to_dev(vc.write_positions), to_dev(vc.commit_counts)
-    packed_q = torch.empty((b, h, r, d), dtype=torch.bfloat16, device=dev)
-    packed_k = torch.empty((b, hk, klen, d), dtype=torch.bfloat16, device=dev)
-    packed_v = torch.empty_like(packed_k)
-    vmask = torch.empty((b, h, r, klen), dtype=torch.bfloat16, device=dev)
-    vout = torch.empty((b, h, r, d), dtype=torch.float32, device=dev)
-    # packed Q [b, h, r, d] seen as [batch, rows, heads, d]; packed K/V [b, hk, k, d] as [batch, k, hk, d]
-    vq_view, vk_view, vv_view = packed_q.permute(0, 2, 1, 3), packed_k.permute(0, 2, 1, 3), packed_v.permute(0, 2, 1, 3)
-    vo_view = vout.permute(0, 2, 1, 3)
-    vap = fa.prefill_params(vq_view, vk_view, vv_view, vmask, vo_view, scale=vc.scale)
-    vws = torch.empty(max(1, fa.prefill_workspace_bytes(vap)), dtype=torch.uint8, device=dev)
-    L = vc.cache_lengths.astype(np.int64)
-    vis_cache = np.minimum(L, w - 1)
-    pack_bytes = (vc.cur_q.nbytes + vc.cur_k.nbytes + vc.cur_v.nbytes + 8.0 * b
-                  + float(vis_cache.sum()) * hk * d * 2 * 2
-                  + b * h * r * d * 2 + 2.0 * b * hk * klen * d * 2)
-    mask_bytes = 4.0 * b + b * h * r * klen * 2
-    # rows visible per query row: r drafted + min(L, w - 1 - i) cached
-    vis_rows = np.array([[r + min(int(Lb), w - 1 - i) for i in range(r)] for Lb in L])
-    verify_attn_bytes = (b * h * r * d * 2 + b * h * r * d * 4 + b * h * r * klen * 2
-                         + float(np.max(vis_rows, axis=1).sum()) * hk * d * 2 * 2)
-    verify_attn_flops = 4.0 * d * h * float(vis_rows.sum())
-    cnt = np.minimum(vc.commit_counts.astype(np.int64), vc.max_commit)
-    commit_bytes = float(cnt.sum()) * hk * d * (4 + 2) * 2 + 8.0 * b
+    if vc is not None:
+        vp = fa.DFlashParams(b, h, hk, d, r, w, klen, vc.max_commit)
+        ring_k, ring_v = to_dev(vc.ring_k, True), to_dev(vc.ring_v, True)
+        cq, ck, cv = to_dev(vc.cur_q), to_dev(vc.cur_k), to_dev(vc.cur_v)
+        vL, vwp, vcnt = to_dev(vc.cache_lengths), to_dev(vc.write_positions), to_dev(vc.commit_counts)
+        packed_q = torch.empty((b, h, r, d), dtype=torch.bfloat16, device=dev)
+        packed_k = torch.empty((b, hk, klen, d), dtype=torch.bfloat16, device=dev)
+        packed_v = torch.empty_like(packed_k)
+        vmask = torch.empty((b, h, r, klen), dtype=torch.bfloat16, device=dev)
+        vout = torch.empty((b, h, r, d), dtype=torch.float32, device=dev)
+        # packed Q [b, h, r, d] seen as [batch, rows, heads, d]; packed K/V [b, hk, k, d] as [batch, k, hk, d]
+        vq_view, vk_view, vv_view = (packed_q.permute(0, 2, 1, 3), packed_k.permute(0, 2, 1, 3),
+                                     packed_v.permute(0, 2, 1, 3))
+        vo_view = vout.permute(0, 2, 1, 3)
+        vap = fa.prefill_params(vq_view, vk_view, vv_view, vmask, vo_view, scale=vc.scale)
+        vws = torch.empty(max(1, fa.prefill_workspace_bytes(vap)), dtype=torch.uint8, device=dev)
+        L = vc.cache_lengths.astype(np.int64)
+        vis_cache = np.minimum(L, w - 1)
+        pack_bytes = (vc.cur_q.nbytes + vc.cur_k.nbytes + vc.cur_v.nbytes + 8.0 * b
+                      + float(vis_cache.sum()) * hk * d * 2 * 2
+                      + b * h * r * d * 2 + 2.0 * b * hk * klen * d * 2)
+        mask_bytes = 4.0 * b + b * h * r * klen * 2
+        # rows visible per query row: r drafted + min(L, w - 1 - i) cached
+        vis_rows = np.array([[r + min(int(Lb), w - 1 - i) for i in range(r)] for Lb in L])
+        verify_attn_bytes = (b * h * r * d * 2 + b * h * r * d * 4 + b * h * r * klen * 2
+                             + float(np.max(vis_rows, axis=1).sum()) * hk * d * 2 * 2)
+        verify_attn_flops = 4.0 * d * h * float(vis_rows.sum())
+        cnt = np.minimum(vc.commit_counts.astype(np.int64), vc.max_commit)
+        commit_bytes = float(cnt.sum()) * hk * d * (4 + 2) * 2 + 8.0 * b
 
     stream = torch.cuda.current_stream()
 
@@ -153,16 +159,13 @@ def main():
     def run_commit():
         fa.dflash_commit(vp, ck, cv, vcnt, vwp, ring_k, ring_v)
 
-    rows = [("prefill", run_prefill), ("decode", run_decode), ("pack", run_pack), ("mask", run_mask),
-            ("verify_attn", run_verify_attn), ("commit", run_commit)]
-    if args.rows_only == "prefill":
-        rows = rows[:1]
-    elif args.rows_only == "decode":
-        rows = rows[1:2]
-    elif args.rows_only == "verify":
-        rows = rows[2:]
-    elif args.rows_only == "chunked":
-        rows = []
+    rows = []
+    if "prefill" in want:
+        rows.append(("prefill", run_prefill))
+    if "decode" in want:
+        rows.append(("decode", run_decode))
+    if "verify" in want:
+        rows += [("pack", run_pack), ("mask", run_mask), ("verify_attn", run_verify_attn), ("commit", run_commit)]
 
     events = {name: [] for name, _ in rows}
 
@@ -195,8 +198,9 @@ def main():
     chunk = None
     if args.rows_only in (None, "chunked"):
         print("bench: chunked prefill (d 512)", file=sys.stderr, flush=True)
-        del dkp, dvp
-        torch.cuda.empty_cache()
+        if "decode" in want:
+            del dkp, dvp
+            torch.cuda.empty_cache()
         cc = workloads.prefill_case("chunked8k")
         cq3, ck3, cv3, cm3 = to_dev(cc.q), to_dev(cc.k), to_dev(cc.v), to_dev(cc.mask)
         co3 = torch.empty(cc.q.shape, dtype=torch.float32, device=dev)
@@ -268,7 +272,8 @@ def main():
         "prefill": {"rows": 2048, "kv_len": 2048, "n_heads": 16, "n_kv_heads": 8, "head_dim": 256,
                     "gflop": prefill_flops / 1e9},
         "decode": {"batch": 64, "page_size": 16, "pool_pages": 65536, "n_heads": 32, "n_kv_heads": 8,
-                   "head_dim": 128, "context_tokens": int(ctx.sum()), "gbytes": decode_bytes / 1e9},
+                   "head_dim": 128, "context_tokens": int(ctx.sum()) if "decode" in want else None,
+                   "gbytes": decode_bytes / 1e9 if "decode" in want else None},
         "verify": {"lanes": b, "rows": r, "window": w, "packed_len": klen, "q_heads": h, "kv_heads": hk,
                    "head_dim": d},
         "parallelism": "single GPU",
@@ -284,8 +289,9 @@ def main():
         comps["decode"]["frac"] = comps["decode"]["gbps"] / PEAK_HBM_GBPS
         out["decode_kv_gbps"] = comps["decode"]["gbps"]
         out["roofline_decode"] = roofline_hbm(decode_bytes, avg_ms["decode"])
-    for name, nbytes in (("pack", pack_bytes), ("mask", mask_bytes), ("verify_attn", verify_attn_bytes),
-                         ("commit", commit_bytes)):
+    verify_rows = ((("pack", pack_bytes), ("mask", mask_bytes), ("verify_attn", verify_attn_bytes),
+                    ("commit", commit_bytes)) if "verify" in want else ())
+    for name, nbytes in verify_rows:
         if name in avg_ms:
             comps[name] = {"ms": avg_ms[name], "gbps": nbytes / (avg_ms[name] * 1e-3) / 1e9,
                            "frac": nbytes / (avg_ms[name] * 1e-3) / 1e9 / PEAK_HBM_GBPS, "mbytes": nbytes / 1e6}

@@ -143,8 +143,13 @@ def test_gqa_matches_repeated_kv(orc):
     rep = workloads.PrefillCase("rep", case.q, np.repeat(case.k, 4, axis=2), np.repeat(case.v, 4, axis=2),
                                 case.mask, case.scale, case.kv_len)
     mha = _run(rep)
-    assert_close(gqa, mha.astype(np.float64), "gqa vs mha", tol=1e-5)
+    # The two calls get different launch shapes (query heads per workgroup, keys per
+    # stage), so their probabilities are rounded to f16 against different running
+    # maxima: they agree to the attention bound, not bit for bit.  A wrong KV-head
+    # mapping would be off by O(1).
+    assert_close(gqa, mha.astype(np.float64), "gqa vs mha")
     assert_close(gqa, _oracle(orc, case), "gqa")
+    assert_close(mha, _oracle(orc, rep), "mha")
 
 
 def _sampled_rows(rows, n, seed):
