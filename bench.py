@@ -34,6 +34,22 @@ import numpy as np
 
 PEAK_F16_TFLOPS = 2500.0
 PEAK_HBM_GBPS = 8000.0
+COPY_PROBE_BYTES = 1 << 30
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def measured_traffic(kernel_source: str):
+    """HBM bytes per launch from the committed counter summary, or None when the
+    kernel source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(HERE, "profiles", "paged_decode_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(os.path.join(HERE, "attention_flash_attn_03_amd", "csrc", kernel_source), "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    return rec["bytes_per_launch"] if rec.get("source_sha256") == sha else None
 
 
 def _parse():
@@ -45,6 +61,8 @@ def _parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
     ap.add_argument("--rows-only", choices=["prefill", "decode", "verify", "chunked"], default=None,
                     help="time one row alone (profiling runs)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (the reference for scaling HBM byte counters)")
     return ap.parse_args()
 
 
@@ -181,6 +199,15 @@ def main():
             else:
                 fn()
 
+    if args.copy_probe:
+        # elementwise copy of known size: reads and writes COPY_PROBE_BYTES once per launch
+        src = torch.ones(COPY_PROBE_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     print("bench: warmup", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         step(False)
@@ -289,6 +316,7 @@ def main():
         comps["decode"]["frac"] = comps["decode"]["gbps"] / PEAK_HBM_GBPS
         out["decode_kv_gbps"] = comps["decode"]["gbps"]
         out["roofline_decode"] = roofline_hbm(decode_bytes, avg_ms["decode"])
+        out["roofline_decode"]["traffic"] = measured_traffic("decode.hip")
     verify_rows = ((("pack", pack_bytes), ("mask", mask_bytes), ("verify_attn", verify_attn_bytes),
                     ("commit", commit_bytes)) if "verify" in want else ())
     for name, nbytes in verify_rows:
