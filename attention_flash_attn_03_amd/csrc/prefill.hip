@@ -30,6 +30,8 @@
 //    log-sum-exp combine pass for calls with few query blocks (block verify).
 #include <math.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -122,6 +124,11 @@ __device__ __forceinline__ int v_swz(int row) { return (row & 3) << 2; }
 
 // Row strides (elements) below this keep every offset inside a 64-row stage under 2^32 bytes.
 constexpr int64_t kOff32Stride = (int64_t)1 << 25;
+
+// Raw buffer descriptors (word 3 of the resource) and the cache policy that makes a
+// buffer access coherent at agent scope (sc1).
+constexpr int kRawBufferFlags = 0x00020000;
+constexpr int kAgentCoherent = 16;
 
 constexpr int cgcd(int x, int y) { return y == 0 ? x : cgcd(y, x % y); }
 
@@ -221,6 +228,21 @@ __device__ __forceinline__ float scale_acc(float x, float f) {
     return x;
 }
 
+// Scheduling pattern for a run of N MFMAs that each consume R LDS reads issued in
+// the same block: the reads of the first A MFMAs go first, then every MFMA (M of
+// them per operand group) is followed by the reads of the group A ahead, so the
+// LDS latency hides under the matrix cores instead of stalling each MFMA.
+template <int N, int R, int M, int A>
+__device__ __forceinline__ void lds_ahead_schedule() {
+    __builtin_amdgcn_sched_group_barrier(0x100, R * A, 0);  // LDS reads
+#pragma unroll
+    for (int i = 0; i < N - A; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, M, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, R, 0);  // LDS reads
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, M * A, 0);
+}
+
 // Wait until every vector-memory operation of this wave has landed, then
 // meet the other waves.
 __device__ __forceinline__ void wait_all_barrier() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -266,6 +288,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     constexpr int MI = 2 * NB;                 // mask DMA instructions per query wave per stage
     __shared__ __attribute__((aligned(1024))) uint4v m_lds[HAS_MASK ? 2 * QW * MI * 64 : 1];
 
+    // A WT_ROWS x DS f32 tile per wave for staging rows of O out (and Q in), carved
+    // from the K and V buffers (free before the first stage and after the last): half
+    // the waves in each.  32 rows at once where they fit, else 16 in two passes.
+    constexpr int WT_PER = NW / 2 > 0 ? NW / 2 : 1;  // wave tiles per buffer
+    constexpr int WT_ROWS = (2 * BK * D * 2) / (WT_PER * DS * 4) >= 32 ? 32 : 16;
+    constexpr int WT_BYTES = WT_ROWS * DS * 4;
+    static_assert(WT_PER * WT_BYTES <= 2 * BK * D * 2, "staging tiles fit the K/V buffers");
+    auto wave_tile = [&](int w) -> char * {
+        return (w < WT_PER ? reinterpret_cast<char *>(k_lds) : reinterpret_cast<char *>(v_lds)) + (w % WT_PER) * WT_BYTES;
+    };
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int slice = wave % NS;
@@ -293,11 +325,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
         const int bh = a.blk_heads == 1 ? 0 : hg;
         return (const_u32 *)(a.blk + (((int64_t)b * a.blk_heads + bh) * a.row_blocks + rbx) * a.blk_stride);
     };
-    // stages of a row block that are not skipped, and the stage after the first `cut` of them
-    auto count_stages = [&](const_u32 *row) {
+    // Stages of a row block that are not skipped, and the stage after the first `cut`
+    // of them: the row of tile codes is scanned by the whole wave, one dword (four
+    // codes) per lane, with a wave-wide sum or prefix sum.
+    auto lane_stages = [&](const uint8_t *row, int w) -> int {  // unskipped stages in dword w
         int n = 0;
-        for (int w = 0; w < a.blk_stride / 4; ++w) {
-            const uint32_t word = row[w];
+        if (w < a.blk_stride / 4) {
+            const uint32_t word = reinterpret_cast<const uint32_t *>(row)[w];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int t = 4 * w + j;
@@ -306,19 +340,52 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
         }
         return n;
     };
-    auto stage_after = [&](const_u32 *row, int cut) {
+    auto code_bytes = [&](int rbx) -> const uint8_t * {
+        const int bh = a.blk_heads == 1 ? 0 : hg;
+        return a.blk + (((int64_t)b * a.blk_heads + bh) * a.row_blocks + rbx) * a.blk_stride;
+    };
+    auto count_stages = [&](int rbx) -> int {
+        const uint8_t *row = code_bytes(rbx);
         int n = 0;
-        for (int w = 0; w < a.blk_stride / 4; ++w) {
-            const uint32_t word = row[w];
+        for (int w0 = 0; w0 < a.blk_stride / 4; w0 += 64) n += lane_stages(row, w0 + lane);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = 4 * w + j;
-                if (t < a.kv_tiles && ((word >> (8 * j)) & 0xffu) != TILE_SKIP) {
-                    const int k = min(SPT, n_stages - t * SPT);
-                    if (n + k >= cut) return t * SPT + (cut - n);
-                    n += k;
-                }
+        for (int off = 32; off > 0; off >>= 1) n += __shfl_xor(n, off);
+        return __builtin_amdgcn_readfirstlane(n);
+    };
+    auto stage_after = [&](int rbx, int cut) -> int {
+        const uint8_t *row = code_bytes(rbx);
+        int before = 0;  // unskipped stages in earlier passes
+        for (int w0 = 0; w0 < a.blk_stride / 4; w0 += 64) {
+            const int w = w0 + lane;
+            const int mine = lane_stages(row, w);
+            int incl = mine;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int up = __shfl_up(incl, off);
+                if (lane >= off) incl += up;
             }
+            const uint64_t hit = __ballot(before + incl >= cut);
+            if (hit) {
+                const int L = __builtin_ctzll(hit);
+                // in lane L: walk its four tiles from the count before it
+                int n = before + incl - mine, at = n_stages;
+                if (lane == L) {
+                    const uint32_t word = reinterpret_cast<const uint32_t *>(row)[w];
+                    for (int j = 0; j < 4; ++j) {
+                        const int t = 4 * w + j;
+                        if (t < a.kv_tiles && ((word >> (8 * j)) & 0xffu) != TILE_SKIP) {
+                            const int k = min(SPT, n_stages - t * SPT);
+                            if (n + k >= cut) {
+                                at = t * SPT + (cut - n);
+                                break;
+                            }
+                            n += k;
+                        }
+                    }
+                }
+                return __builtin_amdgcn_readfirstlane(__shfl(at, L));
+            }
+            before += __shfl(incl, 63);
         }
         return n_stages;
     };
@@ -339,11 +406,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
                 pair = idx >> 1;
                 const int side = idx & 1;
                 const int rb_lo = pair, rb_hi = a.row_blocks - 1 - pair;
-                const int w_hi = count_stages(code_row(rb_hi));
-                const int w_lo = count_stages(code_row(rb_lo));
+                const int w_hi = count_stages(rb_hi);
+                const int w_lo = count_stages(rb_lo);
                 const int cut = min((w_hi + w_lo + 1) >> 1, w_hi);
                 const bool shared = cut > 0 && cut < w_hi;
-                const int s_cut = shared ? stage_after(code_row(rb_hi), cut) : n_stages;
+                const int s_cut = shared ? stage_after(rb_hi, cut) : n_stages;
                 beg0 = 0;
                 end0 = n_stages;
                 if (side == 0) {
@@ -379,52 +446,89 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     const bool row_ok = row < a.rows;
     const int row_c = row_ok ? row : a.rows - 1;
 
-    // ---- Q fragment: B operand of S^T = K Q^T, k = slice*DS + 16*ks + 8*half + i
+    // ---- Q fragment: B operand of S^T = K Q^T, k = slice*DS + 16*ks + 8*half + i.
+    // The wave's query rows (its DS columns) are read with one contiguous row segment
+    // per load instruction into its LDS tile, then picked up in fragment order.
     uint4v qf[KSTEPS];
     uint4v qlo[QSPLIT ? KSTEPS : 1];
     {
-        const int dbase = slice * DS + 8 * half;
-        if (a.q_bf16) {
-            const uint16_t *qp = (const uint16_t *)a.q + b * a.q_bs + (int64_t)row_c * a.q_rs + head * a.q_hs + dbase;
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                uint4v raw = *reinterpret_cast<const uint4v *>(qp + 16 * ks);
-                if constexpr (BF16) {
-                    qf[ks] = raw;
-                } else {
-                    uint4v cv;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const float lo = bf16_bits_to_f32((uint16_t)(raw[e] & 0xffffu));
-                        const float hi = bf16_bits_to_f32((uint16_t)(raw[e] >> 16));
-                        cv[e] = pack2(to_kv16<false>(lo), to_kv16<false>(hi));
-                    }
-                    qf[ks] = cv;
-                }
+        char *tile = wave_tile(wave);
+        // rows of the pass go straight into the tile with LDS DMA: instruction `it` fills
+        // 64 consecutive 16-byte slots (QRPI rows); the lane that fills slot j of row tr
+        // fetches chunk j ^ (tr & 15) of that row, so chunk c lands at slot c ^ (tr & 15)
+        auto stage_rows = [&](auto esz_c, int pass) __attribute__((always_inline)) {
+            constexpr int ESZ = decltype(esz_c)::value;
+            constexpr int QCPR = DS * ESZ / 16;       // 16-byte chunks per row
+            constexpr int QRPI = 64 / QCPR;            // rows per load instruction
+            const uint32_t tbase = (uint32_t)(uintptr_t)(lds_void *)tile;
+#pragma unroll 1
+            for (int it = 0; it < WT_ROWS / QRPI; ++it) {
+                const int tr = it * QRPI + lane / QCPR;
+                const int c = (lane % QCPR) ^ (tr & 15);
+                const int sl = qwave * 32 + pass * WT_ROWS + tr;
+                const int rh = h0 + sl / a.rows_per_wg;
+                int rr = rb * a.rows_per_wg + sl % a.rows_per_wg;
+                rr = rr < a.rows ? rr : a.rows - 1;
+                const char *src = reinterpret_cast<const char *>(a.q) +
+                                  (b * a.q_bs + (int64_t)rr * a.q_rs + rh * a.q_hs + slice * DS) * ESZ + c * 16;
+                const uint32_t m0 = __builtin_amdgcn_readfirstlane(tbase + it * 1024);
+                asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory");
             }
-        } else {
-            const float *qp = (const float *)a.q + b * a.q_bs + (int64_t)row_c * a.q_rs + head * a.q_hs + dbase;
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        };
+        const int tr = col % WT_ROWS;
 #pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                const float4v x0 = *reinterpret_cast<const float4v *>(qp + 16 * ks);
-                const float4v x1 = *reinterpret_cast<const float4v *>(qp + 16 * ks + 4);
-                uint4v cv;
-                cv[0] = pack2(to_kv16<BF16>(x0[0]), to_kv16<BF16>(x0[1]));
-                cv[1] = pack2(to_kv16<BF16>(x0[2]), to_kv16<BF16>(x0[3]));
-                cv[2] = pack2(to_kv16<BF16>(x1[0]), to_kv16<BF16>(x1[1]));
-                cv[3] = pack2(to_kv16<BF16>(x1[2]), to_kv16<BF16>(x1[3]));
-                qf[ks] = cv;
-                if constexpr (QSPLIT) {
-                    float rest[8];
+        for (int pass = 0; pass < 32 / WT_ROWS; ++pass) {
+            if (a.q_bf16) {
+                stage_rows(std::integral_constant<int, 2>{}, pass);
+                if (col / WT_ROWS == pass) {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        rest[e] = x0[e] - bf16_bits_to_f32((uint16_t)(cv[e / 2] >> (16 * (e & 1))));
-                        rest[4 + e] = x1[e] - bf16_bits_to_f32((uint16_t)(cv[2 + e / 2] >> (16 * (e & 1))));
+                    for (int ks = 0; ks < KSTEPS; ++ks) {
+                        const int cc = 2 * ks + half;
+                        const uint4v raw = *reinterpret_cast<const uint4v *>(tile + tr * (DS * 2) + ((cc ^ (tr & 15)) * 16));
+                        if constexpr (BF16) {
+                            qf[ks] = raw;
+                        } else {
+                            uint4v cv;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                const float lo = bf16_bits_to_f32((uint16_t)(raw[e] & 0xffffu));
+                                const float hi = bf16_bits_to_f32((uint16_t)(raw[e] >> 16));
+                                cv[e] = pack2(to_kv16<false>(lo), to_kv16<false>(hi));
+                            }
+                            qf[ks] = cv;
+                        }
                     }
-                    qlo[ks] = uint4v{pack2(f32_to_bf16_rne(rest[0]), f32_to_bf16_rne(rest[1])),
-                                     pack2(f32_to_bf16_rne(rest[2]), f32_to_bf16_rne(rest[3])),
-                                     pack2(f32_to_bf16_rne(rest[4]), f32_to_bf16_rne(rest[5])),
-                                     pack2(f32_to_bf16_rne(rest[6]), f32_to_bf16_rne(rest[7]))};
+                }
+            } else {
+                stage_rows(std::integral_constant<int, 4>{}, pass);
+                if (col / WT_ROWS == pass) {
+#pragma unroll
+                    for (int ks = 0; ks < KSTEPS; ++ks) {
+                        const int cc = 4 * ks + 2 * half;
+                        const float4v x0 =
+                            *reinterpret_cast<const float4v *>(tile + tr * (DS * 4) + ((cc ^ (tr & 15)) * 16));
+                        const float4v x1 =
+                            *reinterpret_cast<const float4v *>(tile + tr * (DS * 4) + (((cc + 1) ^ (tr & 15)) * 16));
+                        uint4v cv;
+                        cv[0] = pack2(to_kv16<BF16>(x0[0]), to_kv16<BF16>(x0[1]));
+                        cv[1] = pack2(to_kv16<BF16>(x0[2]), to_kv16<BF16>(x0[3]));
+                        cv[2] = pack2(to_kv16<BF16>(x1[0]), to_kv16<BF16>(x1[1]));
+                        cv[3] = pack2(to_kv16<BF16>(x1[2]), to_kv16<BF16>(x1[3]));
+                        qf[ks] = cv;
+                        if constexpr (QSPLIT) {
+                            float rest[8];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                rest[e] = x0[e] - bf16_bits_to_f32((uint16_t)(cv[e / 2] >> (16 * (e & 1))));
+                                rest[4 + e] = x1[e] - bf16_bits_to_f32((uint16_t)(cv[2 + e / 2] >> (16 * (e & 1))));
+                            }
+                            qlo[ks] = uint4v{pack2(f32_to_bf16_rne(rest[0]), f32_to_bf16_rne(rest[1])),
+                                             pack2(f32_to_bf16_rne(rest[2]), f32_to_bf16_rne(rest[3])),
+                                             pack2(f32_to_bf16_rne(rest[4]), f32_to_bf16_rne(rest[5])),
+                                             pack2(f32_to_bf16_rne(rest[6]), f32_to_bf16_rne(rest[7]))};
+                        }
+                    }
                 }
             }
         }
@@ -435,6 +539,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
                 if constexpr (QSPLIT) qlo[ks] = qf[ks];
             }
         }
+        __syncthreads();  // every wave has its Q before the first K/V stage overwrites the tiles
     }
 
     const uint16_t *mrow = nullptr;
@@ -565,6 +670,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
                 if constexpr (QSPLIT) s[bb] = mfma32<BF16>(kf, qlo[ks], s[bb]);
             }
         }
+        lds_ahead_schedule<NB * KSTEPS, 1, QSPLIT ? 2 : 1, 6>();
 
         // ---- scale and mask; this lane holds keys key0 + 32*bb + 8*(r/4) + 4*half + r%4
         if (use_mask) {
@@ -667,12 +773,17 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
                 acc_o[db] = mfma32<BF16>(vf, pb[u], acc_o[db]);
             }
         }
+        lds_ahead_schedule<2 * NB * DBLK, 2, 1, 6>();
         lds_done_barrier();  // every wave is done with this stage's buffers
         buf ^= 1;
         st = nxt;
     }
 
-    // ---- epilogue: this lane holds O^T columns query `col`, rows d = slice*DS + 32*db + 8*(r/4) + 4*half + r%4
+    // ---- epilogue: this lane holds O^T columns query `col`, rows d = slice*DS + 32*db + 8*(r/4) + 4*half + r%4.
+    // Split and pair partials are kept in this fragment order (each store instruction
+    // writes 1 KB contiguous); rows of O and of the split partials go out through an
+    // LDS tile of the wave (the K/V buffers are free now), one contiguous row segment
+    // per store instruction.
     bool write_final = a.splits == 1;
     if constexpr (HAS_MASK) {
         if (side >= 0) {
@@ -683,65 +794,103 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
             int *arrival = reinterpret_cast<int *>(m_lds + QW * MI * 64);
             const int slots = a.rows_per_wg * a.heads_per_wg;
             const int64_t pu = ((int64_t)b * a.head_groups + hg) * (a.row_blocks >> 1) + pair;
-            float *mine = a.pair_part + ((pu * 2 + side) * slots + slot) * D + slice * DS + 4 * half;
+            // The two sides may run on different XCDs, whose L2 caches are not coherent
+            // with each other: the partials are written and read with agent-coherent
+            // (sc1) accesses, and only the arrival counter orders them, so no fence has
+            // to write back or invalidate a whole L2.
+            constexpr int PBYTES = DBLK * 4 * 64 * 16;  // one wave's partial
+            const __amdgpu_buffer_rsrc_t mine = __builtin_amdgcn_make_buffer_rsrc(
+                a.pair_part + ((pu * 2 + side) * NW + wave) * (PBYTES / 4), 0, PBYTES, kRawBufferFlags);
 #pragma unroll
             for (int db = 0; db < DBLK; ++db)
 #pragma unroll
                 for (int r4 = 0; r4 < 4; ++r4)
-                    *reinterpret_cast<float4v *>(mine + 32 * db + 8 * r4) =
-                        float4v{acc_o[db][4 * r4], acc_o[db][4 * r4 + 1], acc_o[db][4 * r4 + 2], acc_o[db][4 * r4 + 3]};
-            if (slice == 0 && half == 0) a.pair_ml[(pu * 2 + side) * slots + slot] = make_float2(m_run, l_run);
-            __threadfence();
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        __builtin_bit_cast(uint4v, float4v{acc_o[db][4 * r4], acc_o[db][4 * r4 + 1], acc_o[db][4 * r4 + 2],
+                                                           acc_o[db][4 * r4 + 3]}),
+                        mine, ((db * 4 + r4) * 64 + lane) * 16, 0, kAgentCoherent);
+            if (slice == 0 && half == 0) {
+                __hip_atomic_store(&a.pair_ml[(pu * 2 + side) * slots + slot].x, m_run, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(&a.pair_ml[(pu * 2 + side) * slots + slot].y, l_run, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+            }
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial is out
             __syncthreads();
-            if (threadIdx.x == 0) *arrival = (int)atomicAdd(a.pair_cnt + pu, 1u);
+            if (threadIdx.x == 0)
+                *arrival = (int)__hip_atomic_fetch_add(a.pair_cnt + pu, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __syncthreads();
             write_final = *arrival == 1;
             if (write_final) {
-                __threadfence();
+                // the other side's partial was complete before its increment, which this
+                // side's increment has observed
                 const int other = 1 - side;
-                const float2 mlo = a.pair_ml[(pu * 2 + other) * slots + slot];
-                const float mx = fmaxf(m_run, mlo.x);
+                const float mo = __hip_atomic_load(&a.pair_ml[(pu * 2 + other) * slots + slot].x, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+                const float lo = __hip_atomic_load(&a.pair_ml[(pu * 2 + other) * slots + slot].y, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+                const float mx = fmaxf(m_run, mo);
                 const float wa = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
-                const float wb = mlo.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mlo.x - mx);
-                const float *theirs = a.pair_part + ((pu * 2 + other) * slots + slot) * D + slice * DS + 4 * half;
+                const float wb = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - mx);
+                const __amdgpu_buffer_rsrc_t theirs = __builtin_amdgcn_make_buffer_rsrc(
+                    a.pair_part + ((pu * 2 + other) * NW + wave) * (PBYTES / 4), 0, PBYTES, kRawBufferFlags);
 #pragma unroll
                 for (int db = 0; db < DBLK; ++db)
 #pragma unroll
                     for (int r4 = 0; r4 < 4; ++r4) {
-                        const float4v x = *reinterpret_cast<const float4v *>(theirs + 32 * db + 8 * r4);
+                        const float4v x = __builtin_bit_cast(
+                            float4v, __builtin_amdgcn_raw_buffer_load_b128(theirs, ((db * 4 + r4) * 64 + lane) * 16, 0,
+                                                                           kAgentCoherent));
 #pragma unroll
                         for (int e = 0; e < 4; ++e) acc_o[db][4 * r4 + e] = acc_o[db][4 * r4 + e] * wa + x[e] * wb;
                     }
-                l_run = wa * l_run + wb * mlo.y;
+                l_run = wa * l_run + wb * lo;
             }
         }
     }
-    if (write_final && row_ok) {
-        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-        float *orow = a.o + b * a.o_bs + (int64_t)row * a.o_rs + head * a.o_hs + slice * DS + 4 * half;
+    if (write_final || a.splits > 1) {
+        // rows of this wave's 32 x DS tile: final O (normalised), or a split partial
+        const float sc = write_final ? (l_run > 0.f ? 1.f / l_run : 0.f) : 1.f;
+        char *tile = wave_tile(wave);
+        if (!write_final && slice == 0 && half == 0 && row_ok) {
+            const int64_t unit = (((int64_t)split * a.batch + b) * a.n_heads + head) * a.rows + row;
+            a.ml[unit] = make_float2(m_run, l_run);
+        }
+        constexpr int CPR = DS / 4;      // 16-byte chunks per row
+        constexpr int RPI = 64 / CPR;    // rows per store instruction
+        const int c = lane % CPR;
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db)
+        for (int pass = 0; pass < 32 / WT_ROWS; ++pass) {
+            if (col / WT_ROWS == pass) {
+                const int tr = col % WT_ROWS;
 #pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                float4v x;
+                for (int db = 0; db < DBLK; ++db)
 #pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = acc_o[db][4 * r4 + e] * inv;
-                *reinterpret_cast<float4v *>(orow + 32 * db + 8 * r4) = x;
+                    for (int r4 = 0; r4 < 4; ++r4) {
+                        float4v x;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) x[e] = acc_o[db][4 * r4 + e] * sc;
+                        const int cc = 8 * db + 2 * r4 + half;  // 16-byte chunk of the row
+                        *reinterpret_cast<float4v *>(tile + tr * (DS * 4) + ((cc ^ (tr & 15)) * 16)) = x;
+                    }
             }
-    } else if (a.splits > 1 && row_ok) {
-        const int64_t unit = (((int64_t)split * a.batch + b) * a.n_heads + head) * a.rows + row;
-        float *prow = a.part + unit * D + slice * DS + 4 * half;
 #pragma unroll
-        for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                float4v x;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = acc_o[db][4 * r4 + e];
-                *reinterpret_cast<float4v *>(prow + 32 * db + 8 * r4) = x;
+            for (int it = 0; it < WT_ROWS / RPI; ++it) {
+                const int tr = it * RPI + lane / CPR;
+                const int sl = qwave * 32 + pass * WT_ROWS + tr;
+                const int rh = h0 + sl / a.rows_per_wg;
+                const int rr = rb * a.rows_per_wg + sl % a.rows_per_wg;
+                const float4v x = *reinterpret_cast<const float4v *>(tile + tr * (DS * 4) + ((c ^ (tr & 15)) * 16));
+                if (rr < a.rows) {
+                    float *dst = write_final
+                                     ? a.o + b * a.o_bs + (int64_t)rr * a.o_rs + rh * a.o_hs
+                                     : a.part + ((((int64_t)split * a.batch + b) * a.n_heads + rh) * a.rows + rr) * D;
+                    *reinterpret_cast<float4v *>(dst + slice * DS + 4 * c) = x;
+                }
             }
-        if (slice == 0 && half == 0) a.ml[unit] = make_float2(m_run, l_run);
+        }
     }
+    __syncthreads();  // the next task reuses the LDS tiles
     }  // task
 }
 
