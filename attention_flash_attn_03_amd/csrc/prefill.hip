@@ -266,8 +266,11 @@ __device__ __forceinline__ void lds_done_barrier() { asm volatile("s_waitcnt lgk
 // so each stage's loads have a whole stage of compute to land, and no wait for
 // a load the compiler can see ever drains the prefetch (loads retire in order,
 // and the mask loads are always requested before the stage they belong to).
-template <int D, int NW, bool BF16, bool HAS_MASK, bool QSPLIT>
+// MASK: 0 none, 1 f16, 2 bf16
+template <int D, int NW, bool BF16, int MASK, bool QSPLIT>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1))) void prefill_kernel(PrefillArgs a) {
+    constexpr bool HAS_MASK = MASK != 0;
+    constexpr bool MBF16 = MASK == 2;
     constexpr int NS = D > 256 ? 2 : 1;       // head-dim slices
     constexpr int DS = D / NS;                 // columns per wave
     constexpr int KSTEPS = DS / 16;            // MFMA k-steps of S over a slice
@@ -449,6 +452,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     // ---- Q fragment: B operand of S^T = K Q^T, k = slice*DS + 16*ks + 8*half + i.
     // The wave's query rows (its DS columns) are read with one contiguous row segment
     // per load instruction into its LDS tile, then picked up in fragment order.
+    // Q is rounded to the K/V type anyway (f16, or a bf16 hi + lo pair), so the score
+    // scale and log2(e) are folded in before rounding; only bf16 Q against bf16 K/V is
+    // used as given (re-rounding would add error) and its scores are scaled after the
+    // MFMA.  With two head-dim slices the scaling stays after the MFMA (measured faster:
+    // it rides along with the exchange of the slices' partial scores).
+    constexpr bool PRESCALE = (!BF16 || QSPLIT) && NS == 1;
+    const float q_scale = PRESCALE ? a.score_scale : 1.f;
+    const float post_scale = PRESCALE ? 1.f : a.score_scale;
     uint4v qf[KSTEPS];
     uint4v qlo[QSPLIT ? KSTEPS : 1];
     {
@@ -492,8 +503,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
                             uint4v cv;
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
-                                const float lo = bf16_bits_to_f32((uint16_t)(raw[e] & 0xffffu));
-                                const float hi = bf16_bits_to_f32((uint16_t)(raw[e] >> 16));
+                                const float lo = bf16_bits_to_f32((uint16_t)(raw[e] & 0xffffu)) * q_scale;
+                                const float hi = bf16_bits_to_f32((uint16_t)(raw[e] >> 16)) * q_scale;
                                 cv[e] = pack2(to_kv16<false>(lo), to_kv16<false>(hi));
                             }
                             qf[ks] = cv;
@@ -507,9 +518,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
                     for (int ks = 0; ks < KSTEPS; ++ks) {
                         const int cc = 4 * ks + 2 * half;
                         const float4v x0 =
-                            *reinterpret_cast<const float4v *>(tile + tr * (DS * 4) + ((cc ^ (tr & 15)) * 16));
+                            *reinterpret_cast<const float4v *>(tile + tr * (DS * 4) + ((cc ^ (tr & 15)) * 16)) * q_scale;
                         const float4v x1 =
-                            *reinterpret_cast<const float4v *>(tile + tr * (DS * 4) + (((cc + 1) ^ (tr & 15)) * 16));
+                            *reinterpret_cast<const float4v *>(tile + tr * (DS * 4) + (((cc + 1) ^ (tr & 15)) * 16)) *
+                            q_scale;
                         uint4v cv;
                         cv[0] = pack2(to_kv16<BF16>(x0[0]), to_kv16<BF16>(x0[1]));
                         cv[1] = pack2(to_kv16<BF16>(x0[2]), to_kv16<BF16>(x0[3]));
@@ -672,26 +684,31 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
         }
         lds_ahead_schedule<NB * KSTEPS, 1, QSPLIT ? 2 : 1, 6>();
 
-        // ---- scale and mask; this lane holds keys key0 + 32*bb + 8*(r/4) + 4*half + r%4
+        // ---- scale and mask (log2 units); this lane holds keys key0 + 32*bb + 8*(r/4) + 4*half + r%4
         if (use_mask) {
             uint2 mcur[NB][4];
             load_mask(mcur, st, buf);
+            auto add_mask = [&](auto bf_c) __attribute__((always_inline)) {
+                constexpr bool MBF = decltype(bf_c)::value;
+#pragma unroll
+                for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const uint32_t word = e < 2 ? mcur[bb][q4].x : mcur[bb][q4].y;
+                            const uint16_t m16 = (uint16_t)(word >> (16 * (e & 1)));
+                            const float mv = MBF ? bf16_bits_to_f32(m16) : f16_bits_to_f32(m16);
+                            const float x = s[bb][4 * q4 + e];
+                            s[bb][4 * q4 + e] = PRESCALE ? fmaf(mv, kLog2e, x) : fmaf(x, post_scale, mv * kLog2e);
+                        }
+            };
+            add_mask(std::integral_constant<bool, MBF16>{});
+        } else if constexpr (!PRESCALE) {
 #pragma unroll
             for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const uint32_t word = e < 2 ? mcur[bb][q4].x : mcur[bb][q4].y;
-                        const uint16_t m16 = (uint16_t)(word >> (16 * (e & 1)));
-                        const float mvf = (a.mask_bf16 ? bf16_bits_to_f32(m16) : f16_bits_to_f32(m16)) * kLog2e;
-                        s[bb][4 * q4 + e] = fmaf(s[bb][4 * q4 + e], a.score_scale, mvf);
-                    }
-        } else {
-#pragma unroll
-            for (int bb = 0; bb < NB; ++bb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[bb][r] *= a.score_scale;
+                for (int r = 0; r < 16; ++r) s[bb][r] *= post_scale;
         }
         if constexpr (NS > 1) {
             // add the other slice's partial scores
@@ -918,43 +935,38 @@ __global__ __launch_bounds__(256) void classify_kernel(PrefillArgs a, uint8_t *b
     const uint16_t neg_inf = a.mask_bf16 ? 0xFF80u : 0xFC00u;
     const int key0 = kt * kTile;
     bool any_visible = false, any_nonzero = false;
-    if (a.mask_vec) {
-        // 16 lanes per 64-key row, 4 keys (8 bytes) per lane, 4 rows per pass
-        const int k4 = key0 + 4 * (lane & 15);
-        for (int s = lane >> 4; s < slots; s += 4) {
+    auto see = [&](uint16_t m16) {
+        any_visible |= m16 != neg_inf;
+        any_nonzero |= (m16 & 0x7fffu) != 0;
+    };
+    if (a.mask_dma && key0 + kTile <= a.kv_len) {
+        // 8 lanes per 64-key row, 8 keys (16 bytes) per lane, 8 rows per pass; all the
+        // loads of a wave are independent and go out together
+        const int k8 = key0 + 8 * (lane & 7);
+#pragma unroll 8
+        for (int s0 = 0; s0 < slots; s0 += 8) {
+            const int s = s0 + (lane >> 3);
             const int head = h0 + s / a.rows_per_wg;
             const int row = rb * a.rows_per_wg + s % a.rows_per_wg;
-            if (row >= a.rows) continue;
-            const uint16_t *mr = mbase + head * a.m_hs + (int64_t)row * a.m_rs;
-            if (k4 + 4 <= a.kv_len) {
-                const uint2 raw = *reinterpret_cast<const uint2 *>(mr + k4);
-                const uint16_t m16[4] = {(uint16_t)(raw.x & 0xffffu), (uint16_t)(raw.x >> 16),
-                                         (uint16_t)(raw.y & 0xffffu), (uint16_t)(raw.y >> 16)};
+            if (s < slots && row < a.rows) {
+                const uint4v raw =
+                    *reinterpret_cast<const uint4v *>(mbase + head * a.m_hs + (int64_t)row * a.m_rs + k8);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    any_visible |= m16[e] != neg_inf;
-                    any_nonzero |= (m16[e] & 0x7fffu) != 0;
-                }
-            } else {
-                for (int e = 0; e < 4; ++e) {
-                    if (k4 + e < a.kv_len) {
-                        const uint16_t m16 = mr[k4 + e];
-                        any_visible |= m16 != neg_inf;
-                        any_nonzero |= (m16 & 0x7fffu) != 0;
-                    }
+                    see((uint16_t)(raw[e] & 0xffffu));
+                    see((uint16_t)(raw[e] >> 16));
                 }
             }
         }
     } else {
+        // any alignment, or the ragged last tile: one key per lane, rows in turn
         const int key = key0 + lane;
         if (key < a.kv_len) {
+#pragma unroll 4
             for (int s = 0; s < slots; ++s) {
                 const int head = h0 + s / a.rows_per_wg;
                 const int row = rb * a.rows_per_wg + s % a.rows_per_wg;
-                if (row >= a.rows) continue;
-                const uint16_t m16 = mbase[head * a.m_hs + (int64_t)row * a.m_rs + key];
-                any_visible |= m16 != neg_inf;
-                any_nonzero |= (m16 & 0x7fffu) != 0;
+                if (row < a.rows) see(mbase[head * a.m_hs + (int64_t)row * a.m_rs + key]);
             }
         }
     }
@@ -997,24 +1009,24 @@ __global__ __launch_bounds__(256) void combine_kernel(PrefillArgs a) {
     *reinterpret_cast<float4v *>(a.o + b * a.o_bs + (int64_t)row * a.o_rs + head * a.o_hs + 4 * d4) = acc * inv;
 }
 
-template <int D, int NW, bool BF16, bool HAS_MASK>
+template <int D, int NW, bool BF16, int MASK>
 hipError_t launch_nw(const PrefillArgs &a, const PrefillPlan *plan, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)plan->head_groups * plan->row_blocks * a.splits * a.batch));
     if constexpr (BF16) {
         if (!a.q_bf16) {
-            hipLaunchKernelGGL((prefill_kernel<D, NW, true, HAS_MASK, true>), grid, dim3(64 * NW), 0, stream, a);
+            hipLaunchKernelGGL((prefill_kernel<D, NW, true, MASK, true>), grid, dim3(64 * NW), 0, stream, a);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((prefill_kernel<D, NW, BF16, HAS_MASK, false>), grid, dim3(64 * NW), 0, stream, a);
+    hipLaunchKernelGGL((prefill_kernel<D, NW, BF16, MASK, false>), grid, dim3(64 * NW), 0, stream, a);
     return hipGetLastError();
 }
 
-template <int D, bool BF16, bool HAS_MASK>
+template <int D, bool BF16, int MASK>
 hipError_t launch_typed(const PrefillArgs &a, const PrefillPlan *plan, hipStream_t stream) {
-    if (plan->waves == 4) return launch_nw<D, 4, BF16, HAS_MASK>(a, plan, stream);
+    if (plan->waves == 4) return launch_nw<D, 4, BF16, MASK>(a, plan, stream);
     if constexpr (D <= 256) {
-        if (plan->waves == 2) return launch_nw<D, 2, BF16, HAS_MASK>(a, plan, stream);
+        if (plan->waves == 2) return launch_nw<D, 2, BF16, MASK>(a, plan, stream);
     }
     return hipErrorInvalidValue;
 }
@@ -1031,9 +1043,13 @@ hipError_t launch_for_dim(const PrefillArgs &a, const PrefillPlan *plan, bool bf
     const bool has_mask = a.mask != nullptr;
     hipError_t err;
     if (bf16) {
-        err = has_mask ? launch_typed<D, true, true>(a, plan, stream) : launch_typed<D, true, false>(a, plan, stream);
+        err = !has_mask ? launch_typed<D, true, 0>(a, plan, stream)
+              : a.mask_bf16 ? launch_typed<D, true, 2>(a, plan, stream)
+                            : launch_typed<D, true, 1>(a, plan, stream);
     } else {
-        err = has_mask ? launch_typed<D, false, true>(a, plan, stream) : launch_typed<D, false, false>(a, plan, stream);
+        err = !has_mask ? launch_typed<D, false, 0>(a, plan, stream)
+              : a.mask_bf16 ? launch_typed<D, false, 2>(a, plan, stream)
+                            : launch_typed<D, false, 1>(a, plan, stream);
     }
     if (err != hipSuccess) return err;
     if (plan->splits > 1) return launch_combine<D>(a, stream);
