@@ -7,7 +7,9 @@ all arithmetic runs in the library's HIP kernels.
     attn_prefill       -- prefill / block-verify attention over a contiguous KV range
     attn_paged_decode  -- single-query attention over a paged KV cache
     dflash_pack, dflash_mask, dflash_commit, dflash_mask_rows -- DFlash2 ring steps
-    dflash_validate, kv_pad, prefill_workspace_bytes, decode_workspace_bytes
+    dflash_verify_attention -- block-verify attention read from the ring in place
+    dflash_validate, kv_pad, prefill_workspace_bytes, decode_workspace_bytes,
+    verify_workspace_bytes
 """
 from __future__ import annotations
 
@@ -22,7 +24,7 @@ from ._ffi import AttnError, DFlashParams, DecodeParams, PrefillParams, check
 __all__ = [
     "AttnError", "DFlashParams", "attn_prefill", "attn_paged_decode", "dflash_pack", "dflash_mask",
     "dflash_commit", "dflash_mask_rows", "dflash_validate", "kv_pad", "prefill_params", "decode_params",
-    "prefill_workspace_bytes", "decode_workspace_bytes",
+    "prefill_workspace_bytes", "decode_workspace_bytes", "dflash_verify_attention", "verify_workspace_bytes",
 ]
 
 _DTYPES = {torch.float32: _ffi.ATTN_F32, torch.float16: _ffi.ATTN_F16, torch.bfloat16: _ffi.ATTN_BF16}
@@ -216,6 +218,33 @@ def dflash_commit(params, new_k, new_v, commit_counts, write_positions, ring_k, 
     _want(ring_k, _U16, "ring_k")
     _want(ring_v, _U16, "ring_v")
     check(_ffi.lib().dflash_commit(ctypes.byref(p), *[t.data_ptr() for t in bufs], _bytes(bufs), _stream(stream)))
+
+
+def verify_workspace_bytes(params) -> int:
+    n = ctypes.c_size_t(0)
+    check(_ffi.lib().dflash_verify_workspace_bytes(ctypes.byref(_dflash(params)), ctypes.byref(n)))
+    return n.value
+
+
+def dflash_verify_attention(params, ring_k, ring_v, cur_q, cur_k, cur_v, cache_lengths, write_positions, out, *,
+                            scale: float, workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out f32 [lanes, q_heads, rows, head_dim] = the block-verify attention over
+    the drafted rows and the ring's visible rows, without packing."""
+    p = _dflash(params)
+    bufs = [ring_k, ring_v, cur_q, cur_k, cur_v, cache_lengths, write_positions, out]
+    _want(ring_k, _U16, "ring_k")
+    _want(ring_v, _U16, "ring_v")
+    for t, n in zip((cur_q, cur_k, cur_v, out), ("cur_q", "cur_k", "cur_v", "out")):
+        _want(t, (torch.float32,), n)
+    _want(cache_lengths, _U32, "cache_lengths")
+    _want(write_positions, _U32, "write_positions")
+    need = verify_workspace_bytes(p)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=out.device)
+    check(_ffi.lib().dflash_verify_attention(ctypes.byref(p), float(scale), *[t.data_ptr() for t in bufs],
+                                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                             _bytes(bufs), _stream(stream)))
+    return out
 
 
 def dflash_mask_rows(lanes: int, rows: int, hidden: int, mask_embedding, draft_input, *, stream=None) -> None:

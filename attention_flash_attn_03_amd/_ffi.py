@@ -60,6 +60,9 @@ SIGNATURES = {
     "dflash_mask": ([ctypes.POINTER(DFlashParams), _vp, _vp, ctypes.POINTER(ctypes.c_uint64), _vp], ctypes.c_int),
     "dflash_commit": ([ctypes.POINTER(DFlashParams)] + [_vp] * 6 + [ctypes.POINTER(ctypes.c_uint64), _vp],
                       ctypes.c_int),
+    "dflash_verify_workspace_bytes": ([ctypes.POINTER(DFlashParams), ctypes.POINTER(_sz)], ctypes.c_int),
+    "dflash_verify_attention": ([ctypes.POINTER(DFlashParams), _f32] + [_vp] * 8 + [_vp, _sz,
+                                ctypes.POINTER(ctypes.c_uint64), _vp], ctypes.c_int),
     "dflash_mask_rows": ([_u32, _u32, _u32, _vp, _vp, ctypes.POINTER(ctypes.c_uint64), _vp], ctypes.c_int),
 }
 

@@ -4,6 +4,7 @@
 // mlx-native 0.18.0 flash_attn_prefill_tensor.rs and 0.21.1
 // dflash2_attention_pack.rs pages validate before encoding; a violation
 // returns ATTN_EINVAL with a message that includes the parameters.
+#include <cmath>
 #include <stdarg.h>
 #include <stdio.h>
 
@@ -189,6 +190,17 @@ int check_dflash(const dflash_params *p, const char *who) {
     return ATTN_OK;
 }
 
+int check_verify(const dflash_params *p, attn::VerifyPlan *plan, const char *who) {
+    int st = check_dflash(p, who);
+    if (st != ATTN_OK) return st;
+    if (p->window > attn::kVerifyMaxWindow)
+        return fail("%s: window %u exceeds %u %s", who, p->window, attn::kVerifyMaxWindow, dflash_dump(p).c_str());
+    attn::plan_verify(p, plan);
+    if ((int64_t)p->kv_heads * plan->qgroups > kMaxGridYZ)
+        return fail("%s: grid too large %s", who, dflash_dump(p).c_str());
+    return ATTN_OK;
+}
+
 struct Need {
     const char *label;
     const void *ptr;
@@ -330,6 +342,40 @@ int dflash_commit(const dflash_params *p, const float *new_k, const float *new_v
     return hip_status(attn::launch_dflash_commit(p, new_k, new_v, commit_counts, write_positions, ring_k, ring_v,
                                                  (hipStream_t)stream),
                       "dflash_commit");
+}
+
+int dflash_verify_workspace_bytes(const dflash_params *p, size_t *bytes) {
+    attn::VerifyPlan plan;
+    int st = check_verify(p, &plan, "dflash_verify_workspace_bytes");
+    if (st != ATTN_OK) return st;
+    if (!bytes) return fail("dflash_verify_workspace_bytes: bytes is NULL");
+    *bytes = plan.workspace_bytes;
+    return ATTN_OK;
+}
+
+int dflash_verify_attention(const dflash_params *p, float scale, const uint16_t *ring_k, const uint16_t *ring_v,
+                            const float *cur_q, const float *cur_k, const float *cur_v,
+                            const uint32_t *cache_lengths, const uint32_t *write_positions, float *out, void *ws,
+                            size_t ws_bytes, const uint64_t *bytes, void *stream) {
+    attn::VerifyPlan plan;
+    int st = check_verify(p, &plan, "dflash_verify_attention");
+    if (st != ATTN_OK) return st;
+    if (!std::isfinite(scale)) return fail("dflash_verify_attention: scale must be finite, got %g", (double)scale);
+    const uint64_t b = p->lanes, h = p->q_heads, hk = p->kv_heads, d = p->head_dim, r = p->rows, w = p->window;
+    const Need needs[] = {
+        {"ring keys", ring_k, b, hk, w, d, 2, 16},          {"ring values", ring_v, b, hk, w, d, 2, 16},
+        {"current queries", cur_q, b, r, h, d, 4, 16},      {"current keys", cur_k, b, r, hk, d, 4, 16},
+        {"current values", cur_v, b, r, hk, d, 4, 16},      {"cache lengths", cache_lengths, b, 0, 0, 0, 4, 4},
+        {"write positions", write_positions, b, 0, 0, 0, 4, 4}, {"output", out, b, h, r, d, 4, 16},
+    };
+    st = check_buffers("dflash_verify_attention", needs, 8, bytes);
+    if (st != ATTN_OK) return st;
+    if (!ws || ws_bytes < plan.workspace_bytes || !aligned(ws, 16))
+        return fail("dflash_verify_attention: workspace needs %zu bytes (16-byte aligned), got %zu",
+                    plan.workspace_bytes, ws ? ws_bytes : (size_t)0);
+    return hip_status(attn::launch_dflash_verify(p, &plan, scale, ring_k, ring_v, cur_q, cur_k, cur_v,
+                                                 cache_lengths, write_positions, out, ws, (hipStream_t)stream),
+                      "dflash_verify_attention");
 }
 
 int dflash_mask_rows(uint32_t lanes, uint32_t rows, uint32_t hidden, const uint16_t *mask_embedding,

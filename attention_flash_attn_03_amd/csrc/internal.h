@@ -57,6 +57,27 @@ hipError_t launch_paged_decode(const attn_decode_params *p, const DecodePlan *pl
                                const void *k_pool, const void *v_pool, const int32_t *page_table,
                                const int32_t *context_lens, float *o, void *ws, hipStream_t stream);
 
+// Pack-free block verify: workgroups per (split, KV head x query-head group,
+// lane); the splits per lane are sized on the device from the cache lengths.
+constexpr int kVerifyTileKeys = 32;          // keys per tile
+constexpr int kVerifyMaxSplits = 32;          // splits per lane at most (bounds the workspace)
+constexpr int kVerifyDefaultWorkgroups = 256;  // busy workgroups the split aims for without a device query
+constexpr uint32_t kVerifyMaxWindow = 1u << 24;
+
+struct VerifyPlan {
+    int group, heads_per_wg, qgroups;  // query heads per KV head, per workgroup, groups per KV head
+    int max_splits, target_wgs;
+    size_t ml_offset, ml_bytes;        // (m, l) [lanes][q_heads][rows][max_splits] float2
+    size_t part_offset, part_bytes;    // O partials [lanes][q_heads][rows][max_splits][head_dim] f32
+    size_t workspace_bytes;
+};
+
+int plan_verify(const dflash_params *p, VerifyPlan *plan);
+hipError_t launch_dflash_verify(const dflash_params *p, const VerifyPlan *plan, float scale,
+                                const uint16_t *ring_k, const uint16_t *ring_v, const float *cur_q,
+                                const float *cur_k, const float *cur_v, const uint32_t *cache_lengths,
+                                const uint32_t *write_positions, float *o, void *ws, hipStream_t stream);
+
 hipError_t launch_dflash_pack(const dflash_params *p, const uint16_t *ring_k, const uint16_t *ring_v,
                               const float *cur_q, const float *cur_k, const float *cur_v,
                               const uint32_t *cache_lengths, const uint32_t *write_positions,

@@ -228,21 +228,6 @@ __device__ __forceinline__ float scale_acc(float x, float f) {
     return x;
 }
 
-// Scheduling pattern for a run of N MFMAs that each consume R LDS reads issued in
-// the same block: the reads of the first A MFMAs go first, then every MFMA (M of
-// them per operand group) is followed by the reads of the group A ahead, so the
-// LDS latency hides under the matrix cores instead of stalling each MFMA.
-template <int N, int R, int M, int A>
-__device__ __forceinline__ void lds_ahead_schedule() {
-    __builtin_amdgcn_sched_group_barrier(0x100, R * A, 0);  // LDS reads
-#pragma unroll
-    for (int i = 0; i < N - A; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, M, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, R, 0);  // LDS reads
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, M * A, 0);
-}
-
 // Wait until every vector-memory operation of this wave has landed, then
 // meet the other waves.
 __device__ __forceinline__ void wait_all_barrier() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }

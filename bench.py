@@ -10,9 +10,15 @@ synthetic input resident in HBM:
            permuted 65536-page pool, 32/8 heads, d 128, f16 K/V
            (split-KV partial pass + log-sum-exp reduce)
   verify   DFlash2 block verify, 4 lanes x 16 drafted rows, ring window 4096,
-           32/8 heads, d 128: pack -> mask -> attention -> commit
+           32/8 heads, d 128: pack -> mask -> attention over the packed
+           buffers, the pack-free verify attention read from the ring in
+           place, then commit
 W untimed steps, then K timed steps bracketed by torch.cuda.synchronize().
-Each row is also timed with HIP events on the stream its kernels run on.
+Each row is timed with HIP events on the stream its kernels run on; a GPU
+sleep ahead of each timed step lets the host enqueue the whole step first,
+so an event pair brackets the GPU time of its call only.  ms_per_step is the
+GPU time from the step's first call to its last; wall_ms_per_step is the
+host clock (sleep included).
 
 Prints ONE JSON line.  `value` is the prefill row's algorithmic TFLOP/s
 (4 * n_heads * head_dim per visible (query, key) pair); the paged-decode
@@ -154,6 +160,11 @@ def main():
         verify_attn_bytes = (b * h * r * d * 2 + b * h * r * d * 4 + b * h * r * klen * 2
                              + float(np.max(vis_rows, axis=1).sum()) * hk * d * 2 * 2)
         verify_attn_flops = 4.0 * d * h * float(vis_rows.sum())
+        vfo = torch.empty((b, h, r, d), dtype=torch.float32, device=dev)
+        vfws = torch.empty(fa.verify_workspace_bytes(vp), dtype=torch.uint8, device=dev)
+        # pack-free verify: current Q/K/V (f32), lengths and positions, the visible ring rows, O (f32)
+        fused_bytes = (vc.cur_q.nbytes + vc.cur_k.nbytes + vc.cur_v.nbytes + 8.0 * b
+                       + float(vis_cache.sum()) * hk * d * 2 * 2 + b * h * r * d * 4)
         cnt = np.minimum(vc.commit_counts.astype(np.int64), vc.max_commit)
         commit_bytes = float(cnt.sum()) * hk * d * (4 + 2) * 2 + 8.0 * b
 
@@ -174,6 +185,9 @@ def main():
     def run_verify_attn():
         fa.attn_prefill(vq_view, vk_view, vv_view, vmask, vo_view, scale=vc.scale, workspace=vws)
 
+    def run_verify_fused():
+        fa.dflash_verify_attention(vp, ring_k, ring_v, cq, ck, cv, vL, vwp, vfo, scale=vc.scale, workspace=vfws)
+
     def run_commit():
         fa.dflash_commit(vp, ck, cv, vcnt, vwp, ring_k, ring_v)
 
@@ -183,11 +197,17 @@ def main():
     if "decode" in want:
         rows.append(("decode", run_decode))
     if "verify" in want:
-        rows += [("pack", run_pack), ("mask", run_mask), ("verify_attn", run_verify_attn), ("commit", run_commit)]
+        rows += [("pack", run_pack), ("mask", run_mask), ("verify_attn", run_verify_attn),
+                 ("verify_fused", run_verify_fused), ("commit", run_commit)]
 
     events = {name: [] for name, _ in rows}
+    head_start = [0]  # GPU sleep (cycles) ahead of each timed step
 
     def step(record):
+        if record and head_start[0]:
+            # keeps the GPU busy while the host enqueues the step, so each call's
+            # event pair brackets its own GPU time and not the host's launch work
+            torch.cuda._sleep(head_start[0])
         for name, fn in rows:
             if record:
                 e0 = torch.cuda.Event(enable_timing=True)
@@ -212,14 +232,29 @@ def main():
     for _ in range(args.warmup):
         step(False)
     torch.cuda.synchronize()
+    # size the head start: twice the host's enqueue time of one step, in sleep cycles
+    t_host = time.perf_counter()
+    step(False)
+    t_host = time.perf_counter() - t_host
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    torch.cuda._sleep(1 << 20)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    cycles_per_ms = (1 << 20) / max(c0.elapsed_time(c1), 1e-3)
+    head_start[0] = int(min(2.0 * t_host * 1e3 + 0.2, 20.0) * cycles_per_ms)
     print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = 1e3 * wall / max(1, args.steps)
     avg_ms = {name: float(np.mean([a.elapsed_time(b_) for a, b_ in ev])) for name, ev in events.items() if ev}
+    # GPU time of a step: first call's start event to the last call's end event
+    first, last = events[rows[0][0]], events[rows[-1][0]]
+    ms_per_step = float(np.mean([a[0].elapsed_time(z[1]) for a, z in zip(first, last)]))
+    wall_ms_per_step = 1e3 * wall / max(1, args.steps)
 
     # ---------------- chunked prefill at head_dim 512, timed on its own (outside the step)
     chunk = None
@@ -291,6 +326,7 @@ def main():
     else:
         out.update({"value": None, "unit": "TFLOP/s"})
     out.update({"n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+                "wall_ms_per_step": wall_ms_per_step,
                 "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f16",
                 "data": "synthetic (seeded; shapes and distributions of the five workloads)"})
     out["config"] = {
@@ -318,13 +354,14 @@ def main():
         out["roofline_decode"] = roofline_hbm(decode_bytes, avg_ms["decode"])
         out["roofline_decode"]["traffic"] = measured_traffic("decode.hip")
     verify_rows = ((("pack", pack_bytes), ("mask", mask_bytes), ("verify_attn", verify_attn_bytes),
-                    ("commit", commit_bytes)) if "verify" in want else ())
+                    ("verify_fused", fused_bytes), ("commit", commit_bytes)) if "verify" in want else ())
     for name, nbytes in verify_rows:
         if name in avg_ms:
             comps[name] = {"ms": avg_ms[name], "gbps": nbytes / (avg_ms[name] * 1e-3) / 1e9,
                            "frac": nbytes / (avg_ms[name] * 1e-3) / 1e9 / PEAK_HBM_GBPS, "mbytes": nbytes / 1e6}
-    if "verify_attn" in comps:
-        comps["verify_attn"]["tflops"] = verify_attn_flops / (avg_ms["verify_attn"] * 1e-3) / 1e12
+    for name in ("verify_attn", "verify_fused"):
+        if name in comps:
+            comps[name]["tflops"] = verify_attn_flops / (avg_ms[name] * 1e-3) / 1e12
     if chunk:
         comps["chunked_prefill_d512"] = chunk
     # `roofline` describes the row that takes the most time in a step

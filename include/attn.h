@@ -186,6 +186,28 @@ int dflash_commit(const dflash_params *p, const float *new_k, const float *new_v
                   const uint32_t *commit_counts, const uint32_t *write_positions,
                   uint16_t *ring_k, uint16_t *ring_v, const uint64_t *bytes, void *stream);
 
+/* Pack-free verify attention: the attention that pack, mask and a masked GQA
+ * attention over the packed buffers compute ([pack], the pack and mask
+ * kernels' key order and visibility rule), read from the ring in place.
+ * For lane b with cache length L and write position wp, query row i of head
+ * h attends over (1) the drafted rows p < rows, bf16 of current K/V row p,
+ * all visible, then (2) ring slot (wp - 1 - j) mod window for
+ * j < min(L, window - 1 - i), newest first:
+ *   out[b,h,i,:] = softmax_j(scale * bf16(cur_q[b,i,h,:]) . k_j) . v_j
+ * with KV head h / (q_heads / kv_heads); out f32 [lanes, q_heads, rows,
+ * head_dim], contiguous.  Ring slots outside a lane's visible range are
+ * never read.  Geometry as dflash_validate, plus window <= 2^24.
+ * ws: caller-owned device workspace of dflash_verify_workspace_bytes bytes
+ * (split partials), 16-byte aligned; its contents need no initialisation.
+ * bytes[8] = byte lengths of ring_k, ring_v, cur_q, cur_k, cur_v,
+ * cache_lengths, write_positions, out.  Asynchronous on `stream`. */
+int dflash_verify_workspace_bytes(const dflash_params *p, size_t *bytes);
+int dflash_verify_attention(const dflash_params *p, float scale, const uint16_t *ring_k,
+                            const uint16_t *ring_v, const float *cur_q, const float *cur_k,
+                            const float *cur_v, const uint32_t *cache_lengths,
+                            const uint32_t *write_positions, float *out, void *ws, size_t ws_bytes,
+                            const uint64_t *bytes, void *stream);
+
 /* Mask rows ([pack], the mask-rows kernel): rows 1..rows-1 of every lane's
  * f32 draft input [lanes*rows, hidden] become the bf16 mask embedding
  * [hidden] widened to f32; row 0 (the anchor) is kept.  Rules ([pack]):

@@ -9,6 +9,7 @@ Functions follow the pages as cited in ``oracle.c``:
   attention        -- O1, batched strided masked GQA (two-pass softmax)
   paged_decode     -- O2, single query over a page table
   dflash_pack/mask/commit/mask_rows -- O3..O5 and the mask-rows step
+  dflash_verify_attention -- O1 over the outputs of O3 and O4 (the verify step)
   bf16_from_f32    -- round-to-nearest-even f32 -> bf16 bits
 """
 from __future__ import annotations
@@ -172,6 +173,19 @@ def dflash_mask(geom, cache_lengths):
     m = np.empty((b, h, r, w - 1 + r), np.uint16)
     lib.oracle_dflash_mask(b, h, r, w, _ptr(L), _ptr(m))
     return m
+
+
+def dflash_verify_attention(geom, ring_k, ring_v, cur_q, cur_k, cur_v, cache_lengths, write_positions, *,
+                            scale: float):
+    """The block-verify attention: pack (O3), mask (O4), then masked GQA
+    attention (O1) over the packed buffers with bf16 Q/K/V and mask, exactly
+    as the pack page's dispatch sequence feeds them.  Returns float64 O
+    [lanes, q_heads, rows, head_dim]."""
+    pq, pk, pv = dflash_pack(geom, ring_k, ring_v, cur_q, cur_k, cur_v, cache_lengths, write_positions)
+    m = dflash_mask(geom, cache_lengths)
+    o = attention(pq.transpose(0, 2, 1, 3), pk.transpose(0, 2, 1, 3), pv.transpose(0, 2, 1, 3), m, scale=scale,
+                  q_bf16=True, kv_bf16=True, mask_bf16=True)
+    return np.ascontiguousarray(o.transpose(0, 2, 1, 3))
 
 
 def dflash_commit(geom, max_commit, new_k, new_v, commit_counts, write_positions, ring_k, ring_v):

@@ -27,7 +27,7 @@ def _header_functions():
 
 def test_exports_every_declared_function(lib):
     names = _header_functions()
-    assert len(names) == 11, names
+    assert len(names) == 13, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(_ffi.SIGNATURES)
@@ -83,6 +83,34 @@ def test_dflash_pack_rejects_wrong_byte_lengths_before_launch(lib):
     st = lib.dflash_pack(ctypes.byref(p), *([fake] * 10), arr, None)
     assert st == _ffi.ATTN_EINVAL
     assert b"packed keys must be 1280 bytes" in lib.attn_last_error()
+
+
+def _verify_call(lib, p, sizes, ws_bytes=1 << 20, scale=1.0):
+    fake = 1 << 20  # never dereferenced: the call must fail in host validation
+    arr = (ctypes.c_uint64 * 8)(*sizes)
+    return lib.dflash_verify_attention(ctypes.byref(p), scale, *([fake] * 8), fake, ws_bytes, arr, None)
+
+
+def test_dflash_verify_rejects_before_launch(lib):
+    p = _ffi.DFlashParams(2, 4, 2, 128, 3, 8, 10, 3)
+    sizes = [2 * 2 * 8 * 128 * 2] * 2 + [2 * 3 * 4 * 128 * 4] + [2 * 3 * 2 * 128 * 4] * 2 + [8, 8] \
+        + [2 * 4 * 3 * 128 * 4]
+    need = ctypes.c_size_t(0)
+    assert lib.dflash_verify_workspace_bytes(ctypes.byref(p), ctypes.byref(need)) == _ffi.ATTN_OK
+    # partials for every (lane, head, row) and split: O [.., head_dim] f32 plus (m, l)
+    assert need.value >= 2 * 4 * 3 * (128 * 4 + 8)
+    bad = list(sizes)
+    bad[7] -= 4
+    assert _verify_call(lib, p, bad) == _ffi.ATTN_EINVAL
+    assert b"output must be" in lib.attn_last_error()
+    assert _verify_call(lib, p, sizes, ws_bytes=need.value - 1) == _ffi.ATTN_EINVAL
+    assert b"workspace" in lib.attn_last_error()
+    assert _verify_call(lib, p, sizes, scale=float("nan")) == _ffi.ATTN_EINVAL
+    big = _ffi.DFlashParams(1, 1, 1, 128, 2, (1 << 24) + 1, (1 << 24) + 2, 2)
+    assert lib.dflash_verify_workspace_bytes(ctypes.byref(big), ctypes.byref(need)) == _ffi.ATTN_EINVAL
+    assert b"window" in lib.attn_last_error()
+    bad_geom = _ffi.DFlashParams(2, 4, 2, 64, 3, 8, 10, 3)
+    assert _verify_call(lib, bad_geom, sizes) == _ffi.ATTN_EINVAL
 
 
 def test_dflash_mask_rows_rules(lib):

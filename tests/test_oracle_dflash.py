@@ -230,3 +230,55 @@ def test_full_size_case_shapes(orc):
     assert pq.shape == (2, 4, 4, 128) and pk.shape == (2, 2, 64 - 1 + 4, 128)
     m = orc.dflash_mask(case.geom, case.cache_lengths)
     assert m.shape == (2, 4, 4, 67) and set(np.unique(m)) <= {0, 0xFF80}
+
+
+# --------------------------------------------------------------------------- verify attention
+def _bits_to_f64(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+@pytest.mark.parametrize("w,r", [(5, 2), (8, 3), (8, 4)])
+def test_verify_attention_matches_direct_softmax(orc, w, r):
+    """The verify step's attention computed per query row straight from rings
+    simulated token by token: row i attends over the drafted rows (bf16 by
+    torch's cast) and the newest cached tokens its window reaches (the j-th
+    newest while j < min(L, w - 1 - i)), softmax in float64 with numpy.  Two
+    lanes in different states; GQA with two query heads per KV head."""
+    d, h, hk = 8, 4, 2
+    g = h // hk
+    rng = np.random.Generator(np.random.PCG64(300 + 10 * w + r))
+    scale = 0.7
+    for start in range(w):
+        for n_tokens in (0, 1, w - 2, w, w + 3):
+            lanes = []
+            for lane in range(2):
+                ring = Ring(w, hk * d, (start + 3 * lane) % w)
+                ring_v = Ring(w, hk * d, (start + 3 * lane) % w)
+                for _ in range(n_tokens + lane):
+                    ring.append(_torch_bf16(rng.standard_normal(hk * d)))
+                    ring_v.append(_torch_bf16(rng.standard_normal(hk * d)))
+                lanes.append((ring, ring_v))
+            rk = np.stack([ln[0].slots.reshape(w, hk, d).transpose(1, 0, 2) for ln in lanes])
+            rv = np.stack([ln[1].slots.reshape(w, hk, d).transpose(1, 0, 2) for ln in lanes])
+            cq = rng.standard_normal((2, r, h, d)).astype(np.float32)
+            ck = rng.standard_normal((2, r, hk, d)).astype(np.float32)
+            cv = rng.standard_normal((2, r, hk, d)).astype(np.float32)
+            L = np.array([min(ln[0].length, w) for ln in lanes], np.uint32)
+            wp = np.array([ln[0].wp for ln in lanes], np.uint32)
+            got = orc.dflash_verify_attention((2, h, hk, d, r, w), rk, rv, cq, ck, cv, L, wp, scale=scale)
+            assert got.shape == (2, h, r, d)
+            for b, (ring, ring_v) in enumerate(lanes):
+                for hh in range(h):
+                    kv = hh // g
+                    for i in range(r):
+                        keys = [_bits_to_f64(_torch_bf16(ck[b, p, kv])) for p in range(r)]
+                        vals = [_bits_to_f64(_torch_bf16(cv[b, p, kv])) for p in range(r)]
+                        for j in range(len(ring.history)):
+                            if j < int(L[b]) and j < w - 1 - i:
+                                keys.append(_bits_to_f64(ring.history[-1 - j].reshape(hk, d)[kv]))
+                                vals.append(_bits_to_f64(ring_v.history[-1 - j].reshape(hk, d)[kv]))
+                        q = _bits_to_f64(_torch_bf16(cq[b, i, hh]))
+                        s = scale * (np.array(keys) @ q)
+                        p = np.exp(s - s.max())
+                        want = (p @ np.array(vals)) / p.sum()
+                        assert np.allclose(got[b, hh, i], want, rtol=1e-12, atol=1e-12), (start, n_tokens, b, hh, i)
