@@ -164,8 +164,7 @@ int check_decode(const attn_decode_params *p, attn::DecodePlan *plan) {
         return fail("attn_paged_decode: KV pools hold %lld elements, the strides need more %s", (long long)p->kv_cap,
                     d);
     attn::plan_decode(p, plan);
-    const int hsplit = plan->group / plan->heads_per_wg;
-    if (plan->max_splits > kMaxGridYZ || p->batch > kMaxGridYZ || (int64_t)p->n_kv_heads * hsplit > (1ll << 31) - 1)
+    if (plan->grid > (1ll << 31) - 1 || (int64_t)p->batch * p->n_heads / 4 + 1 > (1ll << 31) - 1)
         return fail("attn_paged_decode: grid too large %s", d);
     return ATTN_OK;
 }

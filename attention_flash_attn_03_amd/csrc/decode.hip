@@ -8,10 +8,13 @@
 //
 // Design: decode is bound by HBM reads of K and V; the kernel keeps enough
 // bytes in flight and keeps the arithmetic off the vector ALUs.
-//  * Split-KV: workgroup (split, KV head, sequence) walks `chunk` tokens of
-//    one sequence for the query heads of one KV head (each K/V row is read
-//    once for all of them); a second kernel merges the splits with a
-//    log-sum-exp reduction.
+//  * Split-KV on a balanced line: every (sequence, KV head group) unit owns
+//    ceil(context / 32) tiles of 32 tokens; the units are laid end to end and
+//    workgroup g takes tiles [g*per, (g+1)*per) of that line (cutting it at
+//    unit boundaries), so every workgroup streams the same number of K/V bytes
+//    and the busy workgroups are a dense prefix of the grid.  Each K/V row is
+//    read once for all query heads of its KV head; a second kernel merges the
+//    pieces with a log-sum-exp reduction.
 //  * The (up to 16) query heads of a KV head are the 16 columns of a
 //    v_mfma_f32_16x16x32 tile: S^T = K Q^T and O^T = V^T P^T run on the
 //    matrix cores; P^T goes from the S^T accumulators straight into the
@@ -32,8 +35,7 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kTok = 32;      // tokens per wave step
-constexpr int kMaxChunk = 1024;  // tokens per workgroup (split) at most
-constexpr int kPgCap = kMaxChunk + 2;             // page ids of one chunk, any page size
+constexpr int kPgCap = kDecodeTilesPerWorkgroup * kTok + 2;  // page ids of one piece, any page size
 
 struct DecodeArgs {
     const float *q;
@@ -44,7 +46,9 @@ struct DecodeArgs {
     float2 *ml;
     int64_t q_bs, q_hs, o_bs, o_hs, page_stride, token_stride, head_stride;
     int batch, n_heads, group, heads_per_wg, page_size, page_shift, max_pages, num_pages, ctx_cap;
-    int chunk, max_splits;
+    int hgroups;     // workgroup head groups per sequence
+    int per;         // tiles (of kTok tokens) per workgroup
+    int max_splits;  // pieces per unit at most
     float score_scale;
 };
 
@@ -93,6 +97,59 @@ __device__ __forceinline__ float sum_over_rows(float x) {
 }
 
 __device__ __forceinline__ int clamp_ctx(int c, int cap) { return c < 0 ? 0 : (c > cap ? cap : c); }
+
+__device__ __forceinline__ int seq_tiles(const DecodeArgs &a, int b) {
+    return (clamp_ctx(a.context_lens[b], a.ctx_cap) + kTok - 1) / kTok;
+}
+
+// Position of sequence b on the tile line.  Wave-wide: 64 sequences per step,
+// an inclusive scan of their tile counts across the lanes.
+struct SeqLoc {
+    int b, tiles;    // sequence and its tiles per unit
+    int64_t start;   // first tile of the sequence's units on the line
+};
+
+__device__ __forceinline__ int64_t scan_lanes(int64_t x, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int64_t y = __shfl_up(x, off);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// The sequence whose units hold line tile `pos`, searching from sequence b0 whose
+// units start at `base`; false when pos is past the end of the line.
+__device__ bool locate_tile(const DecodeArgs &a, int64_t pos, int b0, int64_t base, SeqLoc &out) {
+    const int lane = threadIdx.x & 63;
+    for (; b0 < a.batch; b0 += 64) {
+        const int bb = b0 + lane;
+        const int t = bb < a.batch ? seq_tiles(a, bb) : 0;
+        const int64_t incl = scan_lanes((int64_t)t * a.hgroups, lane);
+        const int64_t total = __shfl(incl, 63);
+        if (pos < base + total) {
+            const int l = __builtin_ctzll(__ballot(base + incl > pos));
+            out.b = b0 + l;
+            out.tiles = __shfl(t, l);
+            out.start = base + __shfl(incl, l) - (int64_t)out.tiles * a.hgroups;
+            return true;
+        }
+        base += total;
+    }
+    return false;
+}
+
+// Line position of sequence b's first unit (wave-wide).
+__device__ int64_t seq_start(const DecodeArgs &a, int b) {
+    const int lane = threadIdx.x & 63;
+    int64_t base = 0;
+    for (int b0 = 0; b0 < b; b0 += 64) {
+        const int bb = b0 + lane;
+        const int64_t t = bb < b ? (int64_t)seq_tiles(a, bb) * a.hgroups : 0;
+        base += __shfl(scan_lanes(t, lane), 63);
+    }
+    return base;
+}
 
 __device__ __forceinline__ int page_of(const DecodeArgs &a, int t) {
     return a.page_shift >= 0 ? (t >> a.page_shift) : t / a.page_size;
@@ -145,35 +202,25 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs &a, uint16_t *k_tile, 
     }
 }
 
+// One piece: tokens [t0, t1) of sequence b for workgroup head group hg, written
+// as partial `split` of its units.
 template <int D, int NWD, bool BF16>
-__global__ __launch_bounds__(64 * NWD) void decode_partial_kernel(DecodeArgs a) {
+__device__ __forceinline__ void decode_piece(const DecodeArgs &a, uint16_t *kv_lds, int *s_pg, int b, int hg, int t0,
+                                             int t1, int split) {
     constexpr int CH = D / 8;
     constexpr int TILE = kTok * D;             // elements of one 32-token tile
     constexpr int NLD = kTok * CH / 64;        // load instructions per tile per wave
     constexpr int KSTEPS = D / 32;             // MFMA k-steps of S^T
     constexpr int DBLK = D / 16;               // 16-row blocks of O^T
-    __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[NWD * 4 * TILE];   // [wave][buffer][K, V]
-    __shared__ int s_pg[kPgCap];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    // KV head is the fastest-varying workgroup index: the workgroups reading the
-    // slices of the same token records run side by side
-    const int split = blockIdx.y;
     const int hsplit = a.group / a.heads_per_wg;
-    const int kvh = blockIdx.x / hsplit;
-    const int head0 = kvh * a.group + (blockIdx.x % hsplit) * a.heads_per_wg;
-    const int b = blockIdx.z;
-    const int ctx = clamp_ctx(a.context_lens[b], a.ctx_cap);
-    const int t0 = split * a.chunk;
+    const int kvh = hg / hsplit;
+    const int head0 = kvh * a.group + (hg % hsplit) * a.heads_per_wg;
     const int64_t unit0 = (int64_t)b * a.n_heads + head0;
-    if (t0 >= ctx) {
-        if (threadIdx.x < a.heads_per_wg) a.ml[(unit0 + threadIdx.x) * a.max_splits + split] = make_float2(-INFINITY, 0.f);
-        return;
-    }
-    const int t1 = min(t0 + a.chunk, ctx);
 
-    // page ids of this chunk (entries past the context are never read)
+    // page ids of this piece (entries past the context are never read)
     const int pg0 = page_of(a, t0);
     const int npg = page_of(a, t1 - 1) - pg0 + 1;
     for (int i = threadIdx.x; i < npg; i += blockDim.x) {
@@ -339,11 +386,38 @@ __global__ __launch_bounds__(64 * NWD) void decode_partial_kernel(DecodeArgs a) 
         a.part[u * D + d] = accv;
         if (d == 0) a.ml[u] = make_float2(mmax, lsum);
     }
+    __syncthreads();  // the next piece reuses the tiles and page ids
+}
+
+template <int D, int NWD, bool BF16>
+__global__ __launch_bounds__(64 * NWD) void decode_partial_kernel(DecodeArgs a) {
+    constexpr int TILE = kTok * D;
+    __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[NWD * 4 * TILE];   // [wave][buffer][K, V]
+    __shared__ int s_pg[kPgCap];
+
+    // line tiles [r0, r1) of this workgroup, cut at unit boundaries into pieces
+    const int64_t r0 = (int64_t)blockIdx.x * a.per, r1 = r0 + a.per;
+    SeqLoc loc;
+    if (!locate_tile(a, r0, 0, 0, loc)) return;
+    int64_t pos = r0;
+    for (;;) {
+        const int hg = (int)((pos - loc.start) / loc.tiles);
+        const int64_t u0 = loc.start + (int64_t)hg * loc.tiles, u1 = u0 + loc.tiles;
+        const int64_t e = u1 < r1 ? u1 : r1;
+        const int ctx = clamp_ctx(a.context_lens[loc.b], a.ctx_cap);
+        const int t0 = (int)(pos - u0) * kTok;
+        const int t1 = min((int)(e - u0) * kTok, ctx);
+        decode_piece<D, NWD, BF16>(a, kv_lds, s_pg, loc.b, hg, t0, t1, blockIdx.x - (int)(u0 / a.per));
+        pos = e;
+        if (pos >= r1) break;
+        const int64_t seq_end = loc.start + (int64_t)loc.tiles * a.hgroups;
+        if (pos >= seq_end && !locate_tile(a, pos, loc.b + 1, seq_end, loc)) break;
+    }
 }
 
 // One wave per (sequence, query head): O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
-// over the splits the sequence used.  Lanes read the (m, l) of 64 splits at a
-// time; the partials are streamed with coalesced loads.
+// over the pieces of its unit.  Lanes read the (m, l) of 64 pieces at a time;
+// the partials are streamed with coalesced loads, eight pieces in flight.
 template <int D>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
     constexpr int PER_LANE = D / 64;
@@ -351,11 +425,12 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
     const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (unit >= (int64_t)a.batch * a.n_heads) return;
     const int b = unit / a.n_heads, head = unit % a.n_heads;
-    const int ctx = clamp_ctx(a.context_lens[b], a.ctx_cap);
-    int nsplit = (ctx + a.chunk - 1) / a.chunk;
+    const int tiles = seq_tiles(a, b);
+    const int64_t u0 = seq_start(a, b) + (int64_t)(head / a.heads_per_wg) * tiles;
+    int nsplit = tiles == 0 ? 0 : (int)((u0 + tiles - 1) / a.per - u0 / a.per + 1);
     if (nsplit > a.max_splits) nsplit = a.max_splits;
     const float2 *ml = a.ml + unit * a.max_splits;
-    const float *part = a.part + unit * a.max_splits * D;
+    const float *part = a.part + unit * a.max_splits * D + lane * PER_LANE;
 
     float mmax = -INFINITY;
     for (int s = lane; s < nsplit; s += 64) mmax = fmaxf(mmax, ml[s].x);
@@ -370,18 +445,31 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
         for (int s0 = 0; s0 < nsplit; s0 += 64) {
             const int s = s0 + lane;
             const float2 my = s < nsplit ? ml[s] : make_float2(-INFINITY, 0.f);
-            const float w = my.x == -INFINITY ? 0.f : exp2f(my.x - mmax);  // splits that saw no token weigh 0
+            const float w = my.x == -INFINITY ? 0.f : exp2f(my.x - mmax);  // pieces that saw no token weigh 0
             float lw = w * my.y;
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1) lw += __shfl_xor(lw, off);
             lsum += lw;
+            // every piece below nsplit wrote its partial: load eight at a time
             const int n = min(64, nsplit - s0);
-            for (int j = 0; j < n; ++j) {
-                const float wj = __shfl(w, j);
-                if (wj == 0.f) continue;
-                const float *pj = part + (int64_t)(s0 + j) * D + lane * PER_LANE;
+            int j = 0;
+            for (; j + 8 <= n; j += 8) {
+                float v[8][PER_LANE];
 #pragma unroll
-                for (int i = 0; i < PER_LANE; ++i) o[i] = fmaf(wj, pj[i], o[i]);
+                for (int u = 0; u < 8; ++u)
+#pragma unroll
+                    for (int i = 0; i < PER_LANE; ++i) v[u][i] = part[(int64_t)(s0 + j + u) * D + i];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float wj = __shfl(w, j + u);
+#pragma unroll
+                    for (int i = 0; i < PER_LANE; ++i) o[i] = fmaf(wj, v[u][i], o[i]);
+                }
+            }
+            for (; j < n; ++j) {
+                const float wj = __shfl(w, j);
+#pragma unroll
+                for (int i = 0; i < PER_LANE; ++i) o[i] = fmaf(wj, part[(int64_t)(s0 + j) * D + i], o[i]);
             }
         }
     }
@@ -392,12 +480,11 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
 }
 
 template <int D, bool BF16>
-hipError_t launch_typed(const DecodeArgs &a, hipStream_t stream) {
+hipError_t launch_typed(const DecodeArgs &a, int64_t grid, hipStream_t stream) {
     // one wave per workgroup: 32 KiB (d 128) / 64 KiB (d 256) of double-buffered tiles, so several
     // workgroups share a CU and one's first-tile latency overlaps another's steady state
     constexpr int NWD = 1;
-    dim3 grid((a.n_heads / a.group) * (a.group / a.heads_per_wg), a.max_splits, a.batch);
-    hipLaunchKernelGGL((decode_partial_kernel<D, NWD, BF16>), grid, dim3(64 * NWD), 0, stream, a);
+    hipLaunchKernelGGL((decode_partial_kernel<D, NWD, BF16>), dim3((unsigned)grid), dim3(64 * NWD), 0, stream, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t units = (int64_t)a.batch * a.n_heads;
@@ -414,12 +501,17 @@ int plan_decode(const attn_decode_params *p, DecodePlan *plan) {
     for (int c = 1; c <= 16 && c <= plan->group; ++c)
         if (plan->group % c == 0) gw = c;
     plan->heads_per_wg = gw;
+    plan->hgroups = p->n_kv_heads * (plan->group / gw);
     int cap = p->max_context;
     const int64_t table_cap = (int64_t)p->max_pages_per_seq * p->page_size;
     if (table_cap < cap) cap = (int)table_cap;
-    // tokens per split: long enough to amortise the first tile's latency, short enough to fill the chip
-    plan->chunk = cap <= 2048 ? 128 : (cap <= 4096 ? 256 : (cap <= 8192 ? 512 : kMaxChunk));
-    plan->max_splits = cap > 0 ? (cap + plan->chunk - 1) / plan->chunk : 1;
+    if (cap < 0) cap = 0;
+    const int64_t tiles_max = ((int64_t)cap + kTok - 1) / kTok;
+    plan->per = kDecodeTilesPerWorkgroup;
+    // a unit of T tiles overlaps at most ceil(T / per) + 1 workgroup ranges
+    plan->max_splits = (int)((tiles_max + plan->per - 1) / plan->per + 1);
+    const int64_t line = (int64_t)p->batch * plan->hgroups * tiles_max;
+    plan->grid = line > 0 ? (line + plan->per - 1) / plan->per : 1;
     const size_t units = (size_t)p->batch * p->n_heads;
     plan->ml_offset = 0;
     plan->ml_bytes = units * plan->max_splits * sizeof(float2);
@@ -458,8 +550,9 @@ hipError_t launch_paged_decode(const attn_decode_params *p, const DecodePlan *pl
     int cap = p->max_context;
     const int64_t table_cap = (int64_t)p->max_pages_per_seq * p->page_size;
     if (table_cap < cap) cap = (int)table_cap;
-    a.ctx_cap = cap;
-    a.chunk = plan->chunk;
+    a.ctx_cap = cap < 0 ? 0 : cap;
+    a.hgroups = plan->hgroups;
+    a.per = plan->per;
     a.max_splits = plan->max_splits;
     a.score_scale = p->scale * kLog2e;
     int shift = -1;
@@ -468,8 +561,8 @@ hipError_t launch_paged_decode(const attn_decode_params *p, const DecodePlan *pl
     a.page_shift = shift;
     const bool bf16 = p->kv_dtype == ATTN_BF16;
     switch (p->head_dim) {
-    case 128: return bf16 ? launch_typed<128, true>(a, stream) : launch_typed<128, false>(a, stream);
-    case 256: return bf16 ? launch_typed<256, true>(a, stream) : launch_typed<256, false>(a, stream);
+    case 128: return bf16 ? launch_typed<128, true>(a, plan->grid, stream) : launch_typed<128, false>(a, plan->grid, stream);
+    case 256: return bf16 ? launch_typed<256, true>(a, plan->grid, stream) : launch_typed<256, false>(a, plan->grid, stream);
     default: return hipErrorInvalidValue;
     }
 }

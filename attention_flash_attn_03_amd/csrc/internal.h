@@ -42,11 +42,17 @@ hipError_t launch_prefill(const attn_prefill_params *p, const PrefillPlan *plan,
                           const void *k, const void *v, const void *mask, float *o, void *ws,
                           hipStream_t stream);
 
+// Paged decode: the (sequence, KV head group) units are laid end to end as
+// 32-token tiles and every workgroup takes the same number of them.
+constexpr int kDecodeTilesPerWorkgroup = 32;
+
 struct DecodePlan {
     int head_dim, group;              // query heads per KV head
     int heads_per_wg;                 // query heads one workgroup serves
-    int chunk;                        // tokens per split
-    int max_splits;
+    int hgroups;                      // workgroup head groups per sequence
+    int per;                          // tiles per workgroup
+    int max_splits;                   // pieces per unit at most
+    int64_t grid;                     // workgroups
     size_t part_offset, part_bytes;   // O partials [batch][n_heads][max_splits][D] f32
     size_t ml_offset, ml_bytes;       // (m, l) [batch][n_heads][max_splits] float2
     size_t workspace_bytes;

@@ -44,18 +44,21 @@ COPY_PROBE_BYTES = 1 << 30
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-def measured_traffic(kernel_source: str):
-    """HBM bytes per launch from the committed counter summary, or None when the
-    kernel source has changed since the counters were taken."""
+def measured_traffic():
+    """HBM bytes per paged-decode call from the committed counter summary, or None
+    when a source the kernels are built from has changed since the counters were
+    taken."""
     import hashlib
     path = os.path.join(HERE, "profiles", "paged_decode_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    with open(os.path.join(HERE, "attention_flash_attn_03_amd", "csrc", kernel_source), "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    return rec["bytes_per_launch"] if rec.get("source_sha256") == sha else None
+    h = hashlib.sha256()
+    for src in rec.get("sources", []):
+        with open(os.path.join(HERE, src), "rb") as f:
+            h.update(f.read())
+    return rec["bytes_per_launch"] if rec.get("sources") and h.hexdigest() == rec.get("sources_sha256") else None
 
 
 def _parse():
@@ -352,7 +355,7 @@ def main():
         comps["decode"]["frac"] = comps["decode"]["gbps"] / PEAK_HBM_GBPS
         out["decode_kv_gbps"] = comps["decode"]["gbps"]
         out["roofline_decode"] = roofline_hbm(decode_bytes, avg_ms["decode"])
-        out["roofline_decode"]["traffic"] = measured_traffic("decode.hip")
+        out["roofline_decode"]["traffic"] = measured_traffic()
     verify_rows = ((("pack", pack_bytes), ("mask", mask_bytes), ("verify_attn", verify_attn_bytes),
                     ("verify_fused", fused_bytes), ("commit", commit_bytes)) if "verify" in want else ())
     for name, nbytes in verify_rows:
