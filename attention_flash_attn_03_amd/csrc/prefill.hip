@@ -17,17 +17,23 @@
 //  * O^T = V^T P^T reuses P^T straight from the S^T accumulator registers as
 //    the B operand; V stays row-major in LDS and its transposed A fragments
 //    come from ds_read_b64_tr_b16 (4 keys x 1 column per lane per read).
-//  * K and V tiles (64 rows) stream into LDS with global_load_lds_dwordx4
-//    (no staging registers), XOR-swizzled so both LDS read patterns are free
-//    of bank conflicts.  The loads are offset by half a tile: K(j+1) lands
-//    while softmax and P V of tile j run, V(j+1) while S of tile j+1 runs.
+//  * K and V stages (64 or 32 rows) and the classified mask tiles stream into
+//    LDS with global_load_lds_dwordx4 (no staging registers), XOR-swizzled so
+//    both LDS read patterns are free of bank conflicts.  Stages are double
+//    buffered: stage j+1 is requested right after the barrier that opens
+//    stage j.  Q comes in and O goes out through LDS as whole rows
+//    (coalesced), with the score scale folded into Q where that is exact
+//    enough.
 //  * exp2 with log2(e) folded into the score scale; P is rounded to the K/V
 //    type before P V and the running sum l is taken from the rounded P, so
 //    the rounding cancels in O / l.  O is rescaled only when some lane's
 //    running max moved (lazy rescale).
-//  * Row blocks are dispatched longest first (causal frontiers make the last
-//    blocks the heaviest).  Optional KV split across workgroups with a
-//    log-sum-exp combine pass for calls with few query blocks (block verify).
+//  * Masked calls pair row blocks p and RB-1-p across two workgroups that
+//    split their unskipped stages evenly, whatever the mask shape; the side
+//    that finishes a cut block second merges the two partial results
+//    (agent-coherent buffer accesses and a relaxed atomic counter, no fence).
+//    Calls with few query blocks split the KV range across workgroups with a
+//    log-sum-exp combine pass.
 #include <math.h>
 
 #include <type_traits>
