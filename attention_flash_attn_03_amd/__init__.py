@@ -6,6 +6,7 @@ all arithmetic runs in the library's HIP kernels.
 
     attn_prefill       -- prefill / block-verify attention over a contiguous KV range
     attn_paged_decode  -- single-query attention over a paged KV cache
+    attn_paged_prefill -- multi-token causal attention over a paged KV cache
     dflash_pack, dflash_mask, dflash_commit, dflash_mask_rows -- DFlash2 ring steps
     dflash_verify_attention -- block-verify attention read from the ring in place
     dflash_validate, kv_pad, prefill_workspace_bytes, decode_workspace_bytes,
@@ -19,10 +20,11 @@ from typing import Optional, Sequence
 import torch
 
 from . import _ffi
-from ._ffi import AttnError, DFlashParams, DecodeParams, PrefillParams, check
+from ._ffi import AttnError, DFlashParams, DecodeParams, PagedPrefillParams, PrefillParams, check
 
 __all__ = [
-    "AttnError", "DFlashParams", "attn_prefill", "attn_paged_decode", "dflash_pack", "dflash_mask",
+    "AttnError", "DFlashParams", "attn_prefill", "attn_paged_decode", "attn_paged_prefill", "paged_prefill_params",
+    "paged_prefill_workspace_bytes", "dflash_pack", "dflash_mask",
     "dflash_commit", "dflash_mask_rows", "dflash_validate", "kv_pad", "prefill_params", "decode_params",
     "prefill_workspace_bytes", "decode_workspace_bytes", "dflash_verify_attention", "verify_workspace_bytes",
 ]
@@ -154,6 +156,61 @@ def attn_paged_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tenso
                                        page_table.data_ptr(), context_lens.data_ptr(), out.data_ptr(),
                                        workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                        _stream(stream)))
+    return out
+
+
+# --------------------------------------------------------------------------- multi-token paged attention
+def paged_prefill_params(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, page_table: torch.Tensor,
+                         out: torch.Tensor, *, scale: float, max_context: int) -> PagedPrefillParams:
+    """q, out [B, T, H, D] float32; pools [num_pages, page_size, HK, D] sharing strides; page_table int32 [B, P]."""
+    B, T, H, D = q.shape
+    num_pages, page_size, HK, D2 = k_pool.shape
+    if D2 != D or tuple(v_pool.shape) != tuple(k_pool.shape) or v_pool.stride() != k_pool.stride():
+        raise ValueError("k_pool and v_pool must have the same shape and strides, head_dim matching q")
+    if tuple(out.shape) != (B, T, H, D):
+        raise ValueError("out must have q's shape")
+    if k_pool.dtype != v_pool.dtype or q.dtype != torch.float32 or out.dtype != torch.float32:
+        raise TypeError("q/out must be float32 and the pools share one dtype")
+    if page_table.dtype != torch.int32 or not page_table.is_contiguous() or page_table.shape[0] != B:
+        raise ValueError("page_table must be a contiguous int32 [batch, max_pages] tensor")
+    if q.stride(3) != 1 or out.stride(3) != 1 or k_pool.stride(3) != 1:
+        raise ValueError("head_dim must be contiguous")
+    p = PagedPrefillParams()
+    p.batch, p.n_heads, p.n_kv_heads, p.head_dim = B, H, HK, D
+    p.page_size, p.max_pages_per_seq, p.num_pages, p.max_context = page_size, page_table.shape[1], num_pages, max_context
+    p.max_tokens = T
+    p.kv_dtype = _code(k_pool)
+    p.scale = scale
+    p.q_bs, p.q_ts, p.q_hs = q.stride(0), q.stride(1), q.stride(2)
+    p.o_bs, p.o_ts, p.o_hs = out.stride(0), out.stride(1), out.stride(2)
+    p.kv_page_stride, p.kv_token_stride, p.kv_head_stride = k_pool.stride(0), k_pool.stride(1), k_pool.stride(2)
+    p.q_cap, p.o_cap = _cap(q), _cap(out)
+    p.kv_cap = min(_cap(k_pool), _cap(v_pool))
+    return p
+
+
+def paged_prefill_workspace_bytes(p: PagedPrefillParams) -> int:
+    n = ctypes.c_size_t(0)
+    check(_ffi.lib().attn_paged_prefill_workspace_bytes(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def attn_paged_prefill(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, page_table: torch.Tensor,
+                       query_lens: torch.Tensor, position_starts: torch.Tensor, out: torch.Tensor, *, scale: float,
+                       max_context: int, workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Query token i of sequence b (position position_starts[b] + i) attends to the keys at or
+    before its position; rows i >= query_lens[b] of `out` are left as they are."""
+    p = paged_prefill_params(q, k_pool, v_pool, page_table, out, scale=scale, max_context=max_context)
+    for t, n in ((query_lens, "query_lens"), (position_starts, "position_starts")):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != q.shape[0]:
+            raise ValueError("%s must be a contiguous int32 [batch] tensor" % n)
+    need = paged_prefill_workspace_bytes(p)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    check(_ffi.lib().attn_paged_prefill(ctypes.byref(p), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                        page_table.data_ptr(), query_lens.data_ptr(), position_starts.data_ptr(),
+                                        out.data_ptr(), workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
 
 

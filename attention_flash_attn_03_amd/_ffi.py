@@ -40,6 +40,16 @@ class DecodeParams(ctypes.Structure):
     )
 
 
+class PagedPrefillParams(ctypes.Structure):
+    _fields_ = (
+        [(n, _i32) for n in ("batch", "n_heads", "n_kv_heads", "head_dim", "page_size", "max_pages_per_seq",
+                             "num_pages", "max_context", "max_tokens", "kv_dtype")]
+        + [("scale", _f32)]
+        + [(n, _i64) for n in ("q_bs", "q_ts", "q_hs", "o_bs", "o_ts", "o_hs", "kv_page_stride", "kv_token_stride",
+                               "kv_head_stride", "q_cap", "kv_cap", "o_cap")]
+    )
+
+
 class DFlashParams(ctypes.Structure):
     _fields_ = [(n, _u32) for n in ("lanes", "q_heads", "kv_heads", "head_dim", "rows", "window",
                                     "packed_len", "max_commit")]
@@ -54,6 +64,9 @@ SIGNATURES = {
     "attn_paged_decode_workspace_bytes": ([ctypes.POINTER(DecodeParams), ctypes.POINTER(_sz)], ctypes.c_int),
     "attn_paged_decode": ([ctypes.POINTER(DecodeParams), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                           ctypes.c_int),
+    "attn_paged_prefill_workspace_bytes": ([ctypes.POINTER(PagedPrefillParams), ctypes.POINTER(_sz)],
+                                           ctypes.c_int),
+    "attn_paged_prefill": ([ctypes.POINTER(PagedPrefillParams)] + [_vp] * 7 + [_vp, _sz, _vp], ctypes.c_int),
     "dflash_validate": ([ctypes.POINTER(DFlashParams)], ctypes.c_int),
     "dflash_pack": ([ctypes.POINTER(DFlashParams)] + [_vp] * 10 + [ctypes.POINTER(ctypes.c_uint64), _vp],
                     ctypes.c_int),

@@ -169,6 +169,60 @@ int check_decode(const attn_decode_params *p, attn::DecodePlan *plan) {
     return ATTN_OK;
 }
 
+std::string paged_prefill_dump(const attn_paged_prefill_params *p) {
+    char buf[640];
+    snprintf(buf, sizeof buf,
+             "{batch=%d n_heads=%d n_kv_heads=%d head_dim=%d page_size=%d max_pages_per_seq=%d num_pages=%d "
+             "max_context=%d max_tokens=%d kv_dtype=%d scale=%g q=(%lld,%lld,%lld) o=(%lld,%lld,%lld) "
+             "kv=(%lld,%lld,%lld) caps=(%lld,%lld,%lld)}",
+             p->batch, p->n_heads, p->n_kv_heads, p->head_dim, p->page_size, p->max_pages_per_seq, p->num_pages,
+             p->max_context, p->max_tokens, p->kv_dtype, (double)p->scale, (long long)p->q_bs, (long long)p->q_ts,
+             (long long)p->q_hs, (long long)p->o_bs, (long long)p->o_ts, (long long)p->o_hs,
+             (long long)p->kv_page_stride, (long long)p->kv_token_stride, (long long)p->kv_head_stride,
+             (long long)p->q_cap, (long long)p->kv_cap, (long long)p->o_cap);
+    return buf;
+}
+
+int check_paged_prefill(const attn_paged_prefill_params *p, attn::MultiPlan *plan, const char *who) {
+    if (!p) return fail("%s: params is NULL", who);
+    const std::string dump = paged_prefill_dump(p);
+    const char *d = dump.c_str();
+    if (p->batch <= 0 || p->n_heads <= 0 || p->n_kv_heads <= 0 || p->page_size <= 0 || p->max_pages_per_seq <= 0 ||
+        p->num_pages <= 0 || p->max_context < 0)
+        return fail("%s: empty or negative shape %s", who, d);
+    if (p->max_tokens < 1 || p->max_tokens > attn::kMultiMaxTokens)
+        return fail("%s: max_tokens %d outside [1, %d] %s", who, p->max_tokens, attn::kMultiMaxTokens, d);
+    if (p->n_heads % p->n_kv_heads != 0)
+        return fail("%s: n_heads %d is not a multiple of n_kv_heads %d", who, p->n_heads, p->n_kv_heads);
+    if (p->head_dim != 128 && p->head_dim != 256)
+        return fail("%s: unsupported head_dim %d (128 or 256) %s", who, p->head_dim, d);
+    if (p->kv_dtype != ATTN_F16 && p->kv_dtype != ATTN_BF16) return fail("%s: kv_dtype must be F16 or BF16 %s", who, d);
+    if (!std::isfinite(p->scale)) return fail("%s: scale must be finite %s", who, d);
+    if (p->q_bs < 0 || p->q_ts < 0 || p->q_hs < 0 || p->o_bs < 0 || p->o_ts < 0 || p->o_hs < 0 ||
+        p->kv_page_stride < 0 || p->kv_token_stride < 0 || p->kv_head_stride < 0)
+        return fail("%s: negative stride %s", who, d);
+    if (p->q_bs % 4 || p->q_ts % 4 || p->q_hs % 4 || p->o_bs % 4 || p->o_ts % 4 || p->o_hs % 4)
+        return fail("%s: Q/O strides must be multiples of 4 %s", who, d);
+    if (p->kv_page_stride % 8 || p->kv_token_stride % 8 || p->kv_head_stride % 8)
+        return fail("%s: KV strides must be multiples of 8 (128-bit loads) %s", who, d);
+    int64_t need;
+    if (!extent(&need, {{p->batch, p->q_bs}, {p->max_tokens, p->q_ts}, {p->n_heads, p->q_hs}}, p->head_dim) ||
+        need > p->q_cap)
+        return fail("%s: q holds %lld elements, the strides need more %s", who, (long long)p->q_cap, d);
+    if (!extent(&need, {{p->batch, p->o_bs}, {p->max_tokens, p->o_ts}, {p->n_heads, p->o_hs}}, p->head_dim) ||
+        need > p->o_cap)
+        return fail("%s: out holds %lld elements, the strides need more %s", who, (long long)p->o_cap, d);
+    if (!extent(&need, {{p->num_pages, p->kv_page_stride}, {p->page_size, p->kv_token_stride},
+                        {p->n_kv_heads, p->kv_head_stride}},
+                p->head_dim) ||
+        need > p->kv_cap)
+        return fail("%s: KV pools hold %lld elements, the strides need more %s", who, (long long)p->kv_cap, d);
+    attn::plan_paged_prefill(p, plan);
+    if (plan->grid > (1ll << 31) - 1 || (int64_t)p->batch * p->max_tokens * p->n_heads / 4 + 1 > (1ll << 31) - 1)
+        return fail("%s: grid too large %s", who, d);
+    return ATTN_OK;
+}
+
 std::string dflash_dump(const dflash_params *p) {
     char buf[256];
     snprintf(buf, sizeof buf,
@@ -286,6 +340,34 @@ int attn_paged_decode(const attn_decode_params *p, const float *q, const void *k
     return hip_status(attn::launch_paged_decode(p, &plan, q, k_pool, v_pool, page_table, context_lens, o, ws,
                                                 (hipStream_t)stream),
                       "attn_paged_decode");
+}
+
+int attn_paged_prefill_workspace_bytes(const attn_paged_prefill_params *p, size_t *bytes) {
+    attn::MultiPlan plan;
+    int st = check_paged_prefill(p, &plan, "attn_paged_prefill_workspace_bytes");
+    if (st != ATTN_OK) return st;
+    if (!bytes) return fail("attn_paged_prefill_workspace_bytes: bytes is NULL");
+    *bytes = plan.workspace_bytes;
+    return ATTN_OK;
+}
+
+int attn_paged_prefill(const attn_paged_prefill_params *p, const float *q, const void *k_pool, const void *v_pool,
+                       const int32_t *page_table, const int32_t *query_lens, const int32_t *position_starts,
+                       float *o, void *ws, size_t ws_bytes, void *stream) {
+    attn::MultiPlan plan;
+    int st = check_paged_prefill(p, &plan, "attn_paged_prefill");
+    if (st != ATTN_OK) return st;
+    if (!q || !k_pool || !v_pool || !page_table || !query_lens || !position_starts || !o)
+        return fail("attn_paged_prefill: every buffer must be non-NULL");
+    if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(o, 16) ||
+        !aligned(page_table, 4) || !aligned(query_lens, 4) || !aligned(position_starts, 4))
+        return fail("attn_paged_prefill: q, pools and out must be 16-byte aligned, tables 4-byte aligned");
+    if (!ws || ws_bytes < plan.workspace_bytes || !aligned(ws, 16))
+        return fail("attn_paged_prefill: workspace needs %zu bytes (16-byte aligned), got %zu", plan.workspace_bytes,
+                    ws ? ws_bytes : (size_t)0);
+    return hip_status(attn::launch_paged_prefill(p, &plan, q, k_pool, v_pool, page_table, query_lens, position_starts,
+                                                 o, ws, (hipStream_t)stream),
+                      "attn_paged_prefill");
 }
 
 int dflash_validate(const dflash_params *p) { return check_dflash(p, "dflash_validate"); }

@@ -59,6 +59,28 @@ struct DecodePlan {
 };
 
 int plan_decode(const attn_decode_params *p, DecodePlan *plan);
+
+// Multi-token paged attention: the decode line with up to 64 query columns
+// (heads x tokens) per workgroup.
+constexpr int kMultiMinTilesPerWorkgroup = 16;
+constexpr int kMultiMaxTilesPerWorkgroup = 128;
+constexpr int kMultiDefaultWorkgroups = 256;  // without a device query
+constexpr int kMultiMaxTokens = 64;
+
+struct MultiPlan {
+    int group, heads_per_wg, qgroups, hgroups;
+    int ctx_cap, target, max_splits;
+    int64_t grid;
+    size_t ml_offset, ml_bytes;        // (m, l) [batch][max_tokens][n_heads][max_splits] float2
+    size_t part_offset, part_bytes;    // O partials [batch][max_tokens][n_heads][max_splits][head_dim] f32
+    size_t workspace_bytes;
+};
+
+int plan_paged_prefill(const attn_paged_prefill_params *p, MultiPlan *plan);
+hipError_t launch_paged_prefill(const attn_paged_prefill_params *p, const MultiPlan *plan, const float *q,
+                                const void *k_pool, const void *v_pool, const int32_t *page_table,
+                                const int32_t *query_lens, const int32_t *position_starts, float *o, void *ws,
+                                hipStream_t stream);
 hipError_t launch_paged_decode(const attn_decode_params *p, const DecodePlan *plan, const float *q,
                                const void *k_pool, const void *v_pool, const int32_t *page_table,
                                const int32_t *context_lens, float *o, void *ws, hipStream_t stream);

@@ -26,12 +26,12 @@
 //    tiles are gathered row by row (the ring order wraps) with
 //    global_load_lds_dwordx4 into a ring of XOR-swizzled LDS stages, several
 //    tiles ahead of the one in use.
-//  * S^T = K Q^T and O^T += V^T P^T run as v_mfma_f32_16x16x32; P^T goes from
-//    the S^T accumulators into the B operand as a bf16 hi + lo pair (two
-//    products), V^T fragments come from ds_read_b64_tr_b16.  Only tiles that reach past the shortest row's
-//    frontier evaluate the mask.
+//  * The per-tile step (attend.h): S^T = K Q^T and O^T += V^T P^T as
+//    v_mfma_f32_16x16x32, P as a bf16 hi + lo pair.  Only tiles that reach
+//    past the shortest row's frontier evaluate the mask.
 #include <math.h>
 
+#include "attend.h"
 #include "device_common.h"
 #include "internal.h"
 
@@ -39,7 +39,8 @@ namespace attn {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLazyRescale = 8.f;  // log2 units
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct VerifyArgs {
     const uint16_t *ring_k, *ring_v;
@@ -53,32 +54,6 @@ struct VerifyArgs {
     int max_splits, target_wgs;
     float score_scale;  // scale * log2(e)
 };
-
-typedef __attribute__((address_space(3))) short4v lds_short4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-__device__ __forceinline__ float4v mfma16(uint4v a, uint4v b, float4v c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bhalf8, a), __builtin_bit_cast(bhalf8, b), c,
-                                                   0, 0, 0);
-}
-
-// (x[l], x[l ^ 16]) then (x[l], x[l ^ 32]): the four lanes holding one column
-__device__ __forceinline__ float max_over_col(float x) {
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-    return max_with_other_half(x);
-}
-__device__ __forceinline__ float sum_over_col(float x) {
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-    return sum_with_other_half(x);
-}
-
-// LDS tile layouts (TK key rows x D, chunks of 16 bytes):
-//  K: logical chunk c of row r at physical c ^ (r % 16)   (A-operand reads: 16 rows, one chunk)
-//  V: logical chunk c of row r at physical c ^ 2*(r % 8)   (transposing reads: 8 rows x 2 chunks)
-__device__ __forceinline__ int k_swz(int row) { return row & 15; }
-__device__ __forceinline__ int v_swz(int row) { return (row & 7) << 1; }
 
 // Ring rows any query row of lane b sees: min(L, window - 1).
 __device__ __forceinline__ int reach_of(const VerifyArgs &a, int b) {
@@ -147,8 +122,8 @@ __device__ __forceinline__ void issue_ring(const uint16_t *ring_k, const uint16_
         int rs = wp + window - 1 - j;  // in [wp, wp + window - 1]
         rs = rs >= window ? rs - window : rs;
         const int64_t off = (int64_t)rs * D;
-        const uint16_t *ksrc = ring_k + off + 8 * (pch ^ k_swz(row));
-        const uint16_t *vsrc = ring_v + off + 8 * (pch ^ v_swz(row));
+        const uint16_t *ksrc = ring_k + off + 8 * (pch ^ attend_k_swz(row));
+        const uint16_t *vsrc = ring_v + off + 8 * (pch ^ attend_v_swz(row));
         const uint32_t mk = __builtin_amdgcn_readfirstlane(kb + (i * NWV + wave) * 1024);
         const uint32_t mv = __builtin_amdgcn_readfirstlane(vb + (i * NWV + wave) * 1024);
         asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(mk), "v"(ksrc) : "memory");
@@ -175,8 +150,8 @@ __device__ __forceinline__ void write_drafted(const VerifyArgs &a, int b, int kh
         uint4v kv = uint4v{0u, 0u, 0u, 0u}, vv = kv;
         if (row < a.rows) {
             const int64_t src = (((int64_t)b * a.rows + row) * a.kv_heads + kh) * D;
-            kv = f32x8_to_bf16(a.cur_k + src + 8 * (pch ^ k_swz(row)));
-            vv = f32x8_to_bf16(a.cur_v + src + 8 * (pch ^ v_swz(row)));
+            kv = f32x8_to_bf16(a.cur_k + src + 8 * (pch ^ attend_k_swz(row)));
+            vv = f32x8_to_bf16(a.cur_v + src + 8 * (pch ^ attend_v_swz(row)));
         }
         *reinterpret_cast<uint4v *>(k_tile + row * D + 8 * pch) = kv;
         *reinterpret_cast<uint4v *>(v_tile + row * D + 8 * pch) = vv;
@@ -193,18 +168,6 @@ struct VerifyTiling {
     static constexpr int NGRP = D == 128 ? 3 : 2;
 };
 
-// s_waitcnt vmcnt(n * PER) for n <= 4, the count a compile-time immediate
-template <int PER>
-__device__ __forceinline__ void wait_tiles(int n) {
-    switch (n) {
-    case 0: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
-    case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory"); break;
-    case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER) : "memory"); break;
-    case 3: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PER) : "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * PER) : "memory"); break;
-    }
-}
-
 template <int D, int NWV>
 __global__ __launch_bounds__(64 * NWV * VerifyTiling<D>::TEAMS) void verify_partial_kernel(VerifyArgs a) {
     constexpr int TK = VerifyTiling<D>::TK;          // keys per tile
@@ -215,8 +178,6 @@ __global__ __launch_bounds__(64 * NWV * VerifyTiling<D>::TEAMS) void verify_part
     constexpr int TILE = TK * D;                     // elements of one K (or V) tile
     constexpr int KSTEPS = D / 32;                   // MFMA k-steps of S^T
     constexpr int DBLK = D / 16;                     // 16-row blocks of O^T
-    constexpr int KBLK = TK / 16;                    // 16-key blocks of S^T
-    constexpr int PSTEPS = TK / 32;                  // 32-key k-steps of O^T
     constexpr int NLD = TK * (D / 8) / (64 * NW);    // loads per wave per K (or V) tile
     static_assert((TK * (D / 8)) % (64 * NW) == 0, "tile slots must split evenly over the waves");
     static_assert(TEAMS * (NGRP - 1) <= 4 && TEAMS * (NGRP - 1) * 2 * NLD <= 63, "vmcnt immediates");
@@ -284,7 +245,7 @@ __global__ __launch_bounds__(64 * NWV * VerifyTiling<D>::TEAMS) void verify_part
                 ++n_pro;
             }
         }
-        wait_tiles<2 * NLD>(n_pro);
+        attend_wait_tiles<2 * NLD>(n_pro);
 #pragma unroll
         for (int i = 0; i < 2 * KSTEPS; ++i) asm volatile("" : "+v"(x[i]));
 
@@ -306,16 +267,13 @@ __global__ __launch_bounds__(64 * NWV * VerifyTiling<D>::TEAMS) void verify_part
         for (int db = 0; db < DBLK; ++db) acc[db] = float4v{0.f, 0.f, 0.f, 0.f};
         float m_run = -INFINITY, l_run = 0.f;
 
-        // per-lane pieces of the transposing V read: row kb + j/4, logical chunk 2*db + (j&3)/2, element 4*(j&1)
-        const int v_rsub = lane & 15;
-
         const int ngroups = (t_end - t_begin + TEAMS - 1) / TEAMS;
         int gstage = 0;  // first stage of the group in use
         for (int k = 0; k < ngroups; ++k) {
             // ring tiles issued after group k: up to the end of group k + NGRP - 2
             const int issued_end = min(t_end, t_begin + TEAMS * (k + NGRP - 1));
             const int after = max(0, issued_end - (t_begin + TEAMS * (k + 1)));
-            wait_tiles<2 * NLD>(after);
+            attend_wait_tiles<2 * NLD>(after);
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");  // every wave's part of group k is in
             {
                 // group k + NGRP - 1 goes into the stages of group k - 1: every wave is past it
@@ -331,146 +289,18 @@ __global__ __launch_bounds__(64 * NWV * VerifyTiling<D>::TEAMS) void verify_part
             }
             const int t = t_begin + TEAMS * k + team;
             if (t < t_end) {
+                // tile 0 is the drafted rows (keys p < rows visible to every column); ring
+                // tile t holds keys j = TK*(t-1) + k, visible to a column while j < its reach
                 const uint16_t *k_tile = kv_lds + (gstage + team) * 2 * TILE;
-                const uint16_t *v_tile = k_tile + TILE;
-
-                // ---- S^T (TK keys x 16 columns): lane holds column `slot`, keys 16*blk + 4*g4 + r
-                // every K fragment of the tile is read before the first product, and the V^T
-                // fragments are read before the softmax, so the LDS latency overlaps other work
-                uint4v kf[KBLK][KSTEPS];
-#pragma unroll
-                for (int blk = 0; blk < KBLK; ++blk) {
-                    const int row = 16 * blk + slot;
-#pragma unroll
-                    for (int ks = 0; ks < KSTEPS; ++ks)
-                        kf[blk][ks] =
-                            *reinterpret_cast<const uint4v *>(k_tile + row * D + 8 * ((4 * ks + g4) ^ k_swz(row)));
-                }
-                float4v s[KBLK];
-#pragma unroll
-                for (int blk = 0; blk < KBLK; ++blk) s[blk] = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < KSTEPS; ++ks)
-#pragma unroll
-                    for (int blk = 0; blk < KBLK; ++blk) s[blk] = mfma16(kf[blk][ks], qf[ks], s[blk]);
-                lds_ahead_schedule<KBLK * KSTEPS, 1, 1, KBLK * KSTEPS>();
-                // V^T fragments (A operand of O^T += V^T P^T), 32 keys per k-step: k slot e < 4 <->
-                // key 32*ps + 4*g4 + e, e >= 4 <-> key 32*ps + 16 + 4*g4 + (e - 4).  A 16-lane group
-                // reads rows kb..kb+3 x 16 columns per ds_read_b64_tr_b16: lane j points at row
-                // kb + j/4, columns 16*db + 4*(j%4), and receives rows kb..kb+3 of column 16*db + j.
-                uint4v vf[PSTEPS][DBLK];
-#pragma unroll
-                for (int pstep = 0; pstep < PSTEPS; ++pstep) {
-                    const int r0 = 32 * pstep + 4 * g4 + (v_rsub >> 2), r1 = r0 + 16;
-                    const uint16_t *v0 = v_tile + r0 * D + 4 * (v_rsub & 1);
-                    const uint16_t *v1 = v_tile + r1 * D + 4 * (v_rsub & 1);
-                    const int c0 = (v_rsub & 3) >> 1;
-#pragma unroll
-                    for (int db = 0; db < DBLK; ++db) {
-                        const int lch = 2 * db + c0;
-                        const short4v lo =
-                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(v0 + 8 * (lch ^ v_swz(r0))));
-                        const short4v hi =
-                            __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)(v1 + 8 * (lch ^ v_swz(r1))));
-                        vf[pstep][db] = uint4v{pack2((uint16_t)lo[0], (uint16_t)lo[1]),
-                                               pack2((uint16_t)lo[2], (uint16_t)lo[3]),
-                                               pack2((uint16_t)hi[0], (uint16_t)hi[1]),
-                                               pack2((uint16_t)hi[2], (uint16_t)hi[3])};
-                    }
-                }
-#pragma unroll
-                for (int blk = 0; blk < KBLK; ++blk) s[blk] *= a.score_scale;
-                if (t == 0) {
-#pragma unroll
-                    for (int blk = 0; blk < KBLK; ++blk)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (16 * blk + 4 * g4 + r >= a.rows) s[blk][r] = -INFINITY;
-                } else if (TK * t > reach_min) {
-                    const int j0 = TK * (t - 1) + 4 * g4;
-#pragma unroll
-                    for (int blk = 0; blk < KBLK; ++blk)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (j0 + 16 * blk + r >= reach_col) s[blk][r] = -INFINITY;
-                }
-
-                // ---- online softmax per column (16 keys here, the rest in lanes ^16, ^32, ^48)
-                float mx = -INFINITY;
-#pragma unroll
-                for (int blk = 0; blk < KBLK; ++blk)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[blk][r]);
-                mx = max_over_col(mx);
-                // The reference max moves only when this tile's max passes it by more than 2^8
-                // (P then stays below 256), so the accumulators are rarely rescaled.
-                const bool grow = mx > m_run + kLazyRescale;
-                if (__ballot(grow)) {
-                    const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - mx) : 1.f;  // 0 when m_run = -inf
-                    m_run = grow ? mx : m_run;
-                    l_run *= alpha;
-#pragma unroll
-                    for (int db = 0; db < DBLK; ++db) acc[db] *= alpha;
-                }
-                const float m_use = m_run == -INFINITY ? 0.f : m_run;  // a column that has seen no visible key yet
-                // P = hi + lo, both bf16 (upper halves of the f32 bits): the product with V keeps
-                // about 16 significant bits of P, so rows that see few keys are not left with
-                // the 2^-9 error of a single bf16 rounding
-                uint32_t phi[4 * KBLK], plo[4 * KBLK];
-                float ps = 0.f;
-#pragma unroll
-                for (int blk = 0; blk < KBLK; ++blk)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const float p = __builtin_amdgcn_exp2f(s[blk][r] - m_use);
-                        ps += p;
-                        const uint32_t hi = __float_as_uint(p) & 0xffff0000u;
-                        phi[4 * blk + r] = hi;
-                        plo[4 * blk + r] = __float_as_uint(p - __uint_as_float(hi)) & 0xffff0000u;
-                    }
-                l_run += sum_over_col(ps);
-
-                // ---- O^T[d][col] += V^T[d][key] P^T[key][col]
-#pragma unroll
-                for (int pstep = 0; pstep < PSTEPS; ++pstep) {
-                    uint4v pb, pl;
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        pb[e] = (phi[8 * pstep + 2 * e] >> 16) | phi[8 * pstep + 2 * e + 1];
-                        pl[e] = (plo[8 * pstep + 2 * e] >> 16) | plo[8 * pstep + 2 * e + 1];
-                    }
-#pragma unroll
-                    for (int db = 0; db < DBLK; ++db) {
-                        acc[db] = mfma16(vf[pstep][db], pb, acc[db]);
-                        acc[db] = mfma16(vf[pstep][db], pl, acc[db]);
-                    }
-                }
+                attend_tile<D, TK, true, false>(k_tile, k_tile + TILE, qf, qf, a.score_scale,
+                                                t == 0 || TK * t > reach_min, t == 0 ? 0 : TK * (t - 1),
+                                                t == 0 ? a.rows : reach_col, acc, m_run, l_run, lane);
             }
             gstage = gstage + TEAMS == NSTAGE ? 0 : gstage + TEAMS;
         }
 
         // ---- merge the teams' states through LDS (the ring is free once every wave is here)
-        if constexpr (TEAMS == 2) {
-            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-            float4v *x_acc = reinterpret_cast<float4v *>(kv_lds);  // [slice][db][lane]
-            float2 *x_ml = reinterpret_cast<float2 *>(x_acc + NWV * DBLK * 64);
-            if (team == 1) {
-#pragma unroll
-                for (int db = 0; db < DBLK; ++db) x_acc[(cw * DBLK + db) * 64 + lane] = acc[db];
-                x_ml[cw * 64 + lane] = make_float2(m_run, l_run);
-            }
-            __syncthreads();
-            if (team == 0) {
-                const float2 o = x_ml[cw * 64 + lane];
-                const float m = fmaxf(m_run, o.x);
-                const float a0 = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m);
-                const float a1 = o.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(o.x - m);
-#pragma unroll
-                for (int db = 0; db < DBLK; ++db) acc[db] = acc[db] * a0 + x_acc[(cw * DBLK + db) * 64 + lane] * a1;
-                l_run = l_run * a0 + o.y * a1;
-                m_run = m;
-            }
-        }
+        if constexpr (TEAMS == 2) attend_merge_teams<D, NWV>(kv_lds, team, cw, lane, acc, m_run, l_run);
 
         // ---- this split's unnormalised O and (m, l) per column
         if (team == 0 && col_ok) {

@@ -13,6 +13,9 @@ synthetic input resident in HBM:
            32/8 heads, d 128: pack -> mask -> attention over the packed
            buffers, the pack-free verify attention read from the ring in
            place, then commit
+  multi    multi-token paged attention: 16 sequences x 16 new tokens over
+           contexts of 1024..8192 tokens in 16-token pages, 32/8 heads, d 128
+           (block verify straight from the page table)
 W untimed steps, then K timed steps bracketed by torch.cuda.synchronize().
 Each row is timed with HIP events on the stream its kernels run on; a GPU
 sleep ahead of each timed step lets the host enqueue the whole step first,
@@ -68,7 +71,7 @@ def _parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle time for the CPU baseline")
-    ap.add_argument("--rows-only", choices=["prefill", "decode", "verify", "chunked"], default=None,
+    ap.add_argument("--rows-only", choices=["prefill", "decode", "verify", "multi", "chunked"], default=None,
                     help="time one row alone (profiling runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (the reference for scaling HBM byte counters)")
@@ -103,7 +106,7 @@ def main():
         return t.to(dev)
 
     print("bench: building inputs", file=sys.stderr, flush=True)
-    want = {"prefill", "decode", "verify"} if args.rows_only is None else {args.rows_only}
+    want = {"prefill", "decode", "verify", "multi"} if args.rows_only is None else {args.rows_only}
     # ---------------- prefill (causal, 2048 x 2048)
     pc = workloads.prefill_case("causal2k")
     m = pc.meta
@@ -171,6 +174,25 @@ def main():
         cnt = np.minimum(vc.commit_counts.astype(np.int64), vc.max_commit)
         commit_bytes = float(cnt.sum()) * hk * d * (4 + 2) * 2 + 8.0 * b
 
+    # ---------------- multi-token paged attention: block verify straight from the page table
+    if "multi" in want:
+        mc = workloads.paged_multi_case(max_tokens=16, batch=16, ctx_lo=1024, ctx_hi=8192, num_pages=8192,
+                                        n_heads=32, n_kv_heads=8, head_dim=128, seed=6, query_lens=np.full(16, 16))
+        mpc = mc.paged
+        mq = to_dev(mc.q)
+        mkp, mvp = to_dev(mpc.k_pool), to_dev(mpc.v_pool)
+        mpt, mql, mst = to_dev(mpc.page_table), to_dev(mc.query_lens), to_dev(mc.position_starts)
+        mo = torch.empty(mc.q.shape, dtype=torch.float32, device=dev)
+        mpp = fa.paged_prefill_params(mq, mkp, mvp, mpt, mo, scale=mpc.scale, max_context=mpc.max_context)
+        mws = torch.empty(fa.paged_prefill_workspace_bytes(mpp), dtype=torch.uint8, device=dev)
+        mctx = mpc.context_lens.astype(np.int64)
+        # K and V rows of every context token, Q and O (f32), the page-table entries, lengths and starts
+        multi_bytes = (float(mctx.sum()) * 8 * 128 * 2 * 2 + 2.0 * mc.q.nbytes
+                       + 4.0 * float(np.sum(-(-mctx // 16))) + 8.0 * len(mctx))
+        # 4 * heads * d per (query token, visible key): token i of a sequence sees start + i + 1 keys
+        multi_flops = 4.0 * 32 * 128 * float(sum(int(st) * int(n) + int(n) * (int(n) + 1) // 2
+                                                 for st, n in zip(mc.position_starts, mc.query_lens)))
+
     stream = torch.cuda.current_stream()
 
     def run_prefill():
@@ -191,6 +213,10 @@ def main():
     def run_verify_fused():
         fa.dflash_verify_attention(vp, ring_k, ring_v, cq, ck, cv, vL, vwp, vfo, scale=vc.scale, workspace=vfws)
 
+    def run_multi():
+        fa.attn_paged_prefill(mq, mkp, mvp, mpt, mql, mst, mo, scale=mpc.scale, max_context=mpc.max_context,
+                              workspace=mws)
+
     def run_commit():
         fa.dflash_commit(vp, ck, cv, vcnt, vwp, ring_k, ring_v)
 
@@ -202,6 +228,8 @@ def main():
     if "verify" in want:
         rows += [("pack", run_pack), ("mask", run_mask), ("verify_attn", run_verify_attn),
                  ("verify_fused", run_verify_fused), ("commit", run_commit)]
+    if "multi" in want:
+        rows.append(("paged_prefill", run_multi))
 
     events = {name: [] for name, _ in rows}
     head_start = [0]  # GPU sleep (cycles) ahead of each timed step
@@ -365,6 +393,13 @@ def main():
     for name in ("verify_attn", "verify_fused"):
         if name in comps:
             comps[name]["tflops"] = verify_attn_flops / (avg_ms[name] * 1e-3) / 1e12
+    if "paged_prefill" in avg_ms:
+        ms = avg_ms["paged_prefill"]
+        comps["paged_prefill"] = {"workload": "16 sequences x 16 new tokens, contexts 1024..8192, 16-token pages, "
+                                              "32/8 heads, d 128, f16 K/V",
+                                  "ms": ms, "gbps": multi_bytes / (ms * 1e-3) / 1e9,
+                                  "frac": multi_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                                  "mbytes": multi_bytes / 1e6, "tflops": multi_flops / (ms * 1e-3) / 1e12}
     if chunk:
         comps["chunked_prefill_d512"] = chunk
     # `roofline` describes the row that takes the most time in a step

@@ -136,6 +136,43 @@ int attn_paged_decode(const attn_decode_params *p, const float *q, const void *k
                       float *o, void *ws, size_t ws_bytes, void *stream);
 
 /* ------------------------------------------------------------------------
+ * Multi-token paged attention ([paged]: `tokens` new tokens from
+ * `position_start`, causal, over the same paged KV layout as decode; the
+ * new tokens' K/V rows are already in the pages).  Query token i of sequence
+ * b (i < query_lens[b] <= max_tokens) sits at position s = position_starts[b]
+ * + i and attends to the keys t <= s of its sequence:
+ *   O[b,i,h,:] = softmax_t(scale * Q[b,i,h,:] . K[b,t,h/g,:]) . V[b,t,h/g,:]
+ * With one token at position context - 1 it is the decode step; with more
+ * it is chunked prefill (at most 64 tokens per sequence per call) or block
+ * verify straight from the page table.
+ * Page addressing, clamping and pool strides as attn_paged_decode; the
+ * context of sequence b is position_starts[b] + query_lens[b], both clamped
+ * (starts to [0, cap], lengths to [0, max_tokens], the context to cap =
+ * min(max_context, max_pages_per_seq * page_size)); page-table entries past
+ * it are never read.  Q, O: F32 [batch, max_tokens, n_heads, head_dim] with
+ * strides (q_bs, q_ts, q_hs), (o_bs, o_ts, o_hs); rows i >= query_lens[b]
+ * of O are not written.  head_dim 128 or 256; 1 <= max_tokens <= 64.
+ * ws: caller-owned device workspace of attn_paged_prefill_workspace_bytes
+ * bytes, 16-byte aligned; its contents need no initialisation.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    int32_t batch, n_heads, n_kv_heads, head_dim;
+    int32_t page_size, max_pages_per_seq, num_pages, max_context, max_tokens;
+    int32_t kv_dtype; /* ATTN_F16 | ATTN_BF16 */
+    float scale;
+    int64_t q_bs, q_ts, q_hs, o_bs, o_ts, o_hs;
+    int64_t kv_page_stride, kv_token_stride, kv_head_stride;
+    int64_t q_cap, kv_cap, o_cap;
+} attn_paged_prefill_params;
+
+int attn_paged_prefill_workspace_bytes(const attn_paged_prefill_params *p, size_t *bytes);
+
+int attn_paged_prefill(const attn_paged_prefill_params *p, const float *q, const void *k_pool,
+                       const void *v_pool, const int32_t *page_table, const int32_t *query_lens,
+                       const int32_t *position_starts, float *o, void *ws, size_t ws_bytes,
+                       void *stream);
+
+/* ------------------------------------------------------------------------
  * DFlash2 block verify ([pack]).  Geometry as DFlash2AttentionPackParams with
  * the same rules ([pack], validate): 1 <= lanes <= 4; heads > 0; q_heads a
  * multiple of kv_heads; head_dim 128 or 256; 2 <= rows <= 16; window > rows;

@@ -8,6 +8,7 @@ it with gcc, loads it with ctypes and converts numpy arguments.
 Functions follow the pages as cited in ``oracle.c``:
   attention        -- O1, batched strided masked GQA (two-pass softmax)
   paged_decode     -- O2, single query over a page table
+  paged_prefill    -- O1 over keys gathered through a page table, causal by position
   dflash_pack/mask/commit/mask_rows -- O3..O5 and the mask-rows step
   dflash_verify_attention -- O1 over the outputs of O3 and O4 (the verify step)
   bf16_from_f32    -- round-to-nearest-even f32 -> bf16 bits
@@ -139,6 +140,32 @@ def paged_decode(q, k_pool, v_pool, page_table, context_lens, *, scale: float, k
         _ptr(q), _dtype_code(q), qs[0], qs[1],
         _ptr(k_pool), _ptr(v_pool), _dtype_code(k_pool, kv_bf16), ps[0], ps[1], ps[2],
         _ptr(page_table), _ptr(context_lens), _ptr(o), H * D, D)
+    return o
+
+
+def paged_prefill(q, k_pool, v_pool, page_table, query_lens, position_starts, *, scale: float, cap: int,
+                  kv_bf16=False):
+    """Multi-token paged attention: query token i of sequence b sits at position
+    s_b + i (s_b = position_starts[b]) and attends to the keys t <= s_b + i of
+    its sequence, key t read from pool page page_table[b, t // P], slot t % P.
+    The keys of the sequence (its context, s_b + query_lens[b], clamped to cap)
+    are gathered, then O1 runs with the causal mask.  Rows i >= query_lens[b]
+    are NaN.  Returns float64 O [B, T, H, D]."""
+    B, T, H, D = q.shape
+    P = k_pool.shape[1]
+    o = np.full((B, T, H, D), np.nan)
+    for b in range(B):
+        n = min(max(int(query_lens[b]), 0), T)
+        if n == 0:
+            continue
+        st = min(max(int(position_starts[b]), 0), cap)
+        ctx = min(st + n, cap)
+        t = np.arange(ctx)
+        pages = np.asarray(page_table)[b, t // P]
+        kb = np.asarray(k_pool)[pages, t % P][None]
+        vb = np.asarray(v_pool)[pages, t % P][None]
+        mask = np.where(t[None, :] <= st + np.arange(n)[:, None], 0.0, -np.inf)[None, None]
+        o[b, :n] = attention(q[b:b + 1, :n], kb, vb, mask, scale=scale, kv_bf16=kv_bf16)[0]
     return o
 
 

@@ -27,7 +27,7 @@ def _header_functions():
 
 def test_exports_every_declared_function(lib):
     names = _header_functions()
-    assert len(names) == 13, names
+    assert len(names) == 15, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(_ffi.SIGNATURES)
@@ -252,3 +252,45 @@ def test_every_geometry_has_a_launch_shape(lib, head_dim):
                          m_cap=rows * 300, o_cap=rows * h * head_dim)
             st = lib.attn_prefill_workspace_bytes(ctypes.byref(p), ctypes.byref(n))
             assert st == _ffi.ATTN_OK, (rows, n_kv, g, lib.attn_last_error())
+
+
+def _paged_prefill(**kw):
+    p = _ffi.PagedPrefillParams()
+    base = dict(batch=2, n_heads=8, n_kv_heads=2, head_dim=128, page_size=16, max_pages_per_seq=8, num_pages=16,
+                max_context=128, max_tokens=16, kv_dtype=_ffi.ATTN_F16, scale=0.1,
+                q_bs=16 * 8 * 128, q_ts=8 * 128, q_hs=128, o_bs=16 * 8 * 128, o_ts=8 * 128, o_hs=128,
+                kv_page_stride=16 * 2 * 128, kv_token_stride=2 * 128, kv_head_stride=128)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(p, k, v)
+    p.q_cap = p.o_cap = 2 * 16 * 8 * 128
+    p.kv_cap = 16 * 16 * 2 * 128
+    return p
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(max_tokens=0), b"max_tokens"), (dict(max_tokens=65), b"max_tokens"), (dict(head_dim=64), b"head_dim"),
+    (dict(n_kv_heads=3), b"multiple"), (dict(kv_dtype=_ffi.ATTN_F32), b"kv_dtype"), (dict(q_ts=8 * 128 + 2), b"4"),
+    (dict(kv_token_stride=2 * 128 + 4), b"multiples of 8"), (dict(q_bs=10 ** 7), b"q holds"),
+    (dict(scale=float("inf")), b"finite"),
+])
+def test_paged_prefill_rejects_before_launch(lib, kw, msg):
+    p = _paged_prefill(**kw)
+    n = ctypes.c_size_t(0)
+    assert lib.attn_paged_prefill_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == _ffi.ATTN_EINVAL
+    assert msg in lib.attn_last_error(), lib.attn_last_error()
+
+
+def test_paged_prefill_workspace_and_buffers(lib):
+    p = _paged_prefill()
+    n = ctypes.c_size_t(0)
+    assert lib.attn_paged_prefill_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == _ffi.ATTN_OK
+    # (m, l) and O partials for every (sequence, token, head) and piece
+    assert n.value >= 2 * 16 * 8 * (128 * 4 + 8)
+    fake = 1 << 20  # never dereferenced: the call must fail in host validation
+    assert lib.attn_paged_prefill(ctypes.byref(p), fake, fake, fake, fake, fake, fake, fake, fake, n.value - 1,
+                                  None) == _ffi.ATTN_EINVAL
+    assert b"workspace" in lib.attn_last_error()
+    assert lib.attn_paged_prefill(ctypes.byref(p), fake, fake, fake, None, fake, fake, fake, fake, n.value,
+                                  None) == _ffi.ATTN_EINVAL
+

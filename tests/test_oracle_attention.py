@@ -233,3 +233,37 @@ def test_paged_equals_contiguous_attention(orc):
         vv = case.v_pool[case.page_table[b, t // 16], t % 16][None]
         c = orc.attention(case.q[b][None, None], kk, vv, None, scale=0.5)
         assert np.array_equal(o[b], c[0, 0])
+
+
+# --------------------------------------------------------------------------- multi-token paged
+@pytest.mark.parametrize("page_size,seed", [(16, 61), (5, 62)])
+def test_paged_prefill_rows_are_decode_steps(orc, page_size, seed):
+    """Token i of a multi-token call is a decode step of the context that ends at
+    it: the paged decode path (keys read slot by slot through the page table in
+    C) with context position_start + i + 1 gives the same row."""
+    mc = workloads.paged_multi_case(max_tokens=6, seed=seed, batch=4, ctx_lo=1, ctx_hi=90, page_size=page_size,
+                                    num_pages=96, n_heads=4, n_kv_heads=2, head_dim=128)
+    pc = mc.paged
+    got = orc.paged_prefill(mc.q, pc.k_pool, pc.v_pool, pc.page_table, mc.query_lens, mc.position_starts,
+                            scale=0.7, cap=pc.max_context)
+    for b in range(4):
+        n = int(mc.query_lens[b])
+        assert np.all(np.isnan(got[b, n:]))
+        for i in range(n):
+            ctx = np.zeros(4, np.int32)
+            ctx[b] = mc.position_starts[b] + i + 1
+            q1 = np.zeros(pc.q.shape, np.float32)
+            q1[b] = mc.q[b, i]
+            dec = orc.paged_decode(q1, pc.k_pool, pc.v_pool, pc.page_table, ctx, scale=0.7)
+            np.testing.assert_allclose(got[b, i], dec[b], rtol=1e-12, atol=1e-12)
+
+
+def test_paged_prefill_one_token_is_decode(orc):
+    pc = workloads.paged_case(batch=3, ctx_lo=1, ctx_hi=70, num_pages=40, n_heads=4, n_kv_heads=1, head_dim=128,
+                              seed=63)
+    q = pc.q[:, None]
+    got = orc.paged_prefill(q, pc.k_pool, pc.v_pool, pc.page_table, np.ones(3, np.int32), pc.context_lens - 1,
+                            scale=pc.scale, cap=pc.max_context)
+    dec = orc.paged_decode(pc.q, pc.k_pool, pc.v_pool, pc.page_table, pc.context_lens, scale=pc.scale)
+    np.testing.assert_allclose(got[:, 0], dec, rtol=1e-12, atol=1e-12)
+

@@ -260,3 +260,31 @@ def dflash_case(*, lanes: int = 4, q_heads: int = 32, kv_heads: int = 8, head_di
         cnt = np.asarray(commit_counts, np.uint32)
     return DFlashCase((b, h, hk, d, r, w), r, ring_k, ring_v, cur_q, cur_k, cur_v, L, wp, cnt,
                       1.0 / math.sqrt(d))
+
+
+# --------------------------------------------------------------------------- multi-token paged
+@dataclass
+class PagedMultiCase:
+    paged: PagedCase
+    q: np.ndarray                # f32 [B, T, H, D]
+    query_lens: np.ndarray       # int32 [B], in [0, T]
+    position_starts: np.ndarray  # int32 [B]: the new tokens are the last query_lens of the context
+
+
+def paged_multi_case(*, max_tokens: int, seed: int = 5, query_lens=None, **paged_kwargs) -> PagedMultiCase:
+    """Multi-token paged attention inputs: a paged decode case whose last
+    query_lens[b] context tokens are the new ones (their K/V already in the
+    pages), query_lens ~ U{1..max_tokens} capped by the context, Q ~ N(0,1)."""
+    pc = paged_case(seed=seed, **paged_kwargs)
+    rng = np.random.Generator(np.random.PCG64([seed, 7]))
+    b = pc.context_lens.shape[0]
+    if query_lens is None:
+        ql = rng.integers(1, max_tokens, size=b, endpoint=True).astype(np.int32)
+    else:
+        ql = np.asarray(query_lens, np.int32)
+    ql = np.minimum(ql, pc.context_lens).astype(np.int32)
+    starts = (pc.context_lens - ql).astype(np.int32)
+    h, d = pc.q.shape[1], pc.q.shape[2]
+    q = normal_f32(b * max_tokens * h * d, [seed, 8]).reshape(b, max_tokens, h, d)
+    return PagedMultiCase(pc, q, ql, starts)
+
