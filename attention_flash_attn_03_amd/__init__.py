@@ -7,6 +7,7 @@ all arithmetic runs in the library's HIP kernels.
     attn_prefill       -- prefill / block-verify attention over a contiguous KV range
     attn_paged_decode  -- single-query attention over a paged KV cache
     attn_paged_prefill -- multi-token causal attention over a paged KV cache
+    attn_paged_prepare -- Q/K RMS norm, rotary embedding, K/V write into the pages
     dflash_pack, dflash_mask, dflash_commit, dflash_mask_rows -- DFlash2 ring steps
     dflash_verify_attention -- block-verify attention read from the ring in place
     dflash_validate, kv_pad, prefill_workspace_bytes, decode_workspace_bytes,
@@ -20,11 +21,11 @@ from typing import Optional, Sequence
 import torch
 
 from . import _ffi
-from ._ffi import AttnError, DFlashParams, DecodeParams, PagedPrefillParams, PrefillParams, check
+from ._ffi import AttnError, DFlashParams, DecodeParams, PagedPrefillParams, PrefillParams, PrepareParams, check
 
 __all__ = [
     "AttnError", "DFlashParams", "attn_prefill", "attn_paged_decode", "attn_paged_prefill", "paged_prefill_params",
-    "paged_prefill_workspace_bytes", "dflash_pack", "dflash_mask",
+    "paged_prefill_workspace_bytes", "attn_paged_prepare", "dflash_pack", "dflash_mask",
     "dflash_commit", "dflash_mask_rows", "dflash_validate", "kv_pad", "prefill_params", "decode_params",
     "prefill_workspace_bytes", "decode_workspace_bytes", "dflash_verify_attention", "verify_workspace_bytes",
 ]
@@ -212,6 +213,60 @@ def attn_paged_prefill(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tens
                                         out.data_ptr(), workspace.data_ptr(),
                                         workspace.numel() * workspace.element_size(), _stream(stream)))
     return out
+
+
+def attn_paged_prepare(q_raw: torch.Tensor, k_raw: torch.Tensor, v_raw: torch.Tensor,
+                       q_norm: Optional[torch.Tensor], k_norm: Optional[torch.Tensor], page_table: torch.Tensor,
+                       query_lens: torch.Tensor, position_starts: torch.Tensor, q_out: torch.Tensor,
+                       k_pool: torch.Tensor, v_pool: torch.Tensor, *, rope_dim: int, rope_theta: float,
+                       rope_interleaved: bool, epsilon: float, max_context: int, stream=None) -> torch.Tensor:
+    """q_raw [B, T, H, >=D], k_raw/v_raw [B, T, HK, >=D] float32; q_norm/k_norm float32 [H|1, D] / [HK|1, D]
+    or None (no norm); q_out [B, T, H, D] float32; pools [num_pages, page_size, HK, D] f16/bf16."""
+    B, T, H, _ = q_raw.shape
+    num_pages, page_size, HK, D = k_pool.shape
+    if tuple(q_out.shape) != (B, T, H, D) or tuple(k_raw.shape[:3]) != (B, T, HK) or \
+            tuple(v_raw.shape[:3]) != (B, T, HK) or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("inconsistent shapes")
+    if v_pool.stride() != k_pool.stride() or k_pool.dtype != v_pool.dtype:
+        raise ValueError("k_pool and v_pool must share strides and dtype")
+    for t, n in ((q_raw, "q_raw"), (k_raw, "k_raw"), (v_raw, "v_raw"), (q_out, "q_out")):
+        _want(t, (torch.float32,), n)
+        if t.stride(3) != 1:
+            raise ValueError("%s: features must be contiguous" % n)
+    for t, n in ((query_lens, "query_lens"), (position_starts, "position_starts")):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != B:
+            raise ValueError("%s must be a contiguous int32 [batch] tensor" % n)
+    if page_table.dtype != torch.int32 or not page_table.is_contiguous() or page_table.shape[0] != B:
+        raise ValueError("page_table must be a contiguous int32 [batch, max_pages] tensor")
+    p = PrepareParams()
+    p.batch, p.n_heads, p.n_kv_heads, p.head_dim, p.max_tokens = B, H, HK, D, T
+    p.rope_dim, p.rope_interleaved, p.qk_norm = rope_dim, int(bool(rope_interleaved)), int(q_norm is not None)
+    p.page_size, p.max_pages_per_seq, p.num_pages, p.max_context = page_size, page_table.shape[1], num_pages, max_context
+    p.kv_dtype = _code(k_pool)
+    p.epsilon, p.rope_theta = epsilon, rope_theta
+    p.qr_bs, p.qr_ts, p.qr_hs = q_raw.stride(0), q_raw.stride(1), q_raw.stride(2)
+    p.kr_bs, p.kr_ts, p.kr_hs = k_raw.stride(0), k_raw.stride(1), k_raw.stride(2)
+    p.vr_bs, p.vr_ts, p.vr_hs = v_raw.stride(0), v_raw.stride(1), v_raw.stride(2)
+    p.qo_bs, p.qo_ts, p.qo_hs = q_out.stride(0), q_out.stride(1), q_out.stride(2)
+    p.kv_page_stride, p.kv_token_stride, p.kv_head_stride = k_pool.stride(0), k_pool.stride(1), k_pool.stride(2)
+    p.qr_cap, p.kr_cap, p.vr_cap, p.qo_cap = _cap(q_raw), _cap(k_raw), _cap(v_raw), _cap(q_out)
+    p.kv_cap = min(_cap(k_pool), _cap(v_pool))
+    qn = kn = None
+    if q_norm is not None:
+        if k_norm is None:
+            raise ValueError("q_norm and k_norm go together")
+        for t, n in ((q_norm, "q_norm"), (k_norm, "k_norm")):
+            _want(t, (torch.float32,), n)
+            if t.dim() != 2 or t.shape[1] != D or t.stride(1) != 1:
+                raise ValueError("%s must be [heads or 1, head_dim] with contiguous features" % n)
+        p.qn_hs = 0 if q_norm.shape[0] == 1 else q_norm.stride(0)
+        p.kn_hs = 0 if k_norm.shape[0] == 1 else k_norm.stride(0)
+        p.qn_cap, p.kn_cap = _cap(q_norm), _cap(k_norm)
+        qn, kn = q_norm.data_ptr(), k_norm.data_ptr()
+    check(_ffi.lib().attn_paged_prepare(ctypes.byref(p), q_raw.data_ptr(), k_raw.data_ptr(), v_raw.data_ptr(), qn, kn,
+                                        page_table.data_ptr(), query_lens.data_ptr(), position_starts.data_ptr(),
+                                        q_out.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), _stream(stream)))
+    return q_out
 
 
 # --------------------------------------------------------------------------- DFlash2 ring steps

@@ -50,6 +50,18 @@ class PagedPrefillParams(ctypes.Structure):
     )
 
 
+class PrepareParams(ctypes.Structure):
+    _fields_ = (
+        [(n, _i32) for n in ("batch", "n_heads", "n_kv_heads", "head_dim", "max_tokens", "rope_dim",
+                             "rope_interleaved", "qk_norm", "page_size", "max_pages_per_seq", "num_pages",
+                             "max_context", "kv_dtype")]
+        + [("epsilon", _f32), ("rope_theta", _f32)]
+        + [(n, _i64) for n in ("qr_bs", "qr_ts", "qr_hs", "kr_bs", "kr_ts", "kr_hs", "vr_bs", "vr_ts", "vr_hs",
+                               "qo_bs", "qo_ts", "qo_hs", "qn_hs", "kn_hs", "kv_page_stride", "kv_token_stride",
+                               "kv_head_stride", "qr_cap", "kr_cap", "vr_cap", "qo_cap", "qn_cap", "kn_cap", "kv_cap")]
+    )
+
+
 class DFlashParams(ctypes.Structure):
     _fields_ = [(n, _u32) for n in ("lanes", "q_heads", "kv_heads", "head_dim", "rows", "window",
                                     "packed_len", "max_commit")]
@@ -67,6 +79,7 @@ SIGNATURES = {
     "attn_paged_prefill_workspace_bytes": ([ctypes.POINTER(PagedPrefillParams), ctypes.POINTER(_sz)],
                                            ctypes.c_int),
     "attn_paged_prefill": ([ctypes.POINTER(PagedPrefillParams)] + [_vp] * 7 + [_vp, _sz, _vp], ctypes.c_int),
+    "attn_paged_prepare": ([ctypes.POINTER(PrepareParams)] + [_vp] * 11 + [_vp], ctypes.c_int),
     "dflash_validate": ([ctypes.POINTER(DFlashParams)], ctypes.c_int),
     "dflash_pack": ([ctypes.POINTER(DFlashParams)] + [_vp] * 10 + [ctypes.POINTER(ctypes.c_uint64), _vp],
                     ctypes.c_int),

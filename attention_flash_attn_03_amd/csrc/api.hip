@@ -223,6 +223,62 @@ int check_paged_prefill(const attn_paged_prefill_params *p, attn::MultiPlan *pla
     return ATTN_OK;
 }
 
+int check_prepare(const attn_paged_prepare_params *p) {
+    if (!p) return fail("attn_paged_prepare: params is NULL");
+    char buf[512];
+    snprintf(buf, sizeof buf,
+             "{batch=%d n_heads=%d n_kv_heads=%d head_dim=%d max_tokens=%d rope_dim=%d interleaved=%d qk_norm=%d "
+             "page_size=%d max_pages_per_seq=%d num_pages=%d max_context=%d kv_dtype=%d eps=%g theta=%g}",
+             p->batch, p->n_heads, p->n_kv_heads, p->head_dim, p->max_tokens, p->rope_dim, p->rope_interleaved,
+             p->qk_norm, p->page_size, p->max_pages_per_seq, p->num_pages, p->max_context, p->kv_dtype,
+             (double)p->epsilon, (double)p->rope_theta);
+    const char *d = buf;
+    if (p->batch <= 0 || p->n_heads <= 0 || p->n_kv_heads <= 0 || p->max_tokens <= 0 || p->page_size <= 0 ||
+        p->max_pages_per_seq <= 0 || p->num_pages <= 0 || p->max_context < 0)
+        return fail("attn_paged_prepare: empty or negative shape %s", d);
+    if (p->n_heads % p->n_kv_heads != 0)
+        return fail("attn_paged_prepare: n_heads %d is not a multiple of n_kv_heads %d", p->n_heads, p->n_kv_heads);
+    if (p->head_dim != 128 && p->head_dim != 256)
+        return fail("attn_paged_prepare: unsupported head_dim %d (128 or 256) %s", p->head_dim, d);
+    if (p->rope_dim <= 0 || p->rope_dim > p->head_dim || p->rope_dim % 2)
+        return fail("attn_paged_prepare: rope_dim must be even and in (0, head_dim] %s", d);
+    if (p->kv_dtype != ATTN_F16 && p->kv_dtype != ATTN_BF16)
+        return fail("attn_paged_prepare: kv_dtype must be F16 or BF16 %s", d);
+    if (!std::isfinite(p->epsilon) || p->epsilon < 0.f || !std::isfinite(p->rope_theta) || p->rope_theta <= 0.f)
+        return fail("attn_paged_prepare: epsilon must be finite and >= 0, rope_theta finite and > 0 %s", d);
+    const int64_t strides[] = {p->qr_bs, p->qr_ts, p->qr_hs, p->kr_bs, p->kr_ts, p->kr_hs, p->vr_bs, p->vr_ts,
+                               p->vr_hs, p->qo_bs, p->qo_ts, p->qo_hs, p->qn_hs, p->kn_hs, p->kv_page_stride,
+                               p->kv_token_stride, p->kv_head_stride};
+    for (int64_t st : strides)
+        if (st < 0) return fail("attn_paged_prepare: negative stride %s", d);
+    int64_t need;
+    const struct {
+        const char *name;
+        int64_t bs, ts, hs, heads, cap;
+    } rows[] = {{"q_raw", p->qr_bs, p->qr_ts, p->qr_hs, p->n_heads, p->qr_cap},
+                {"k_raw", p->kr_bs, p->kr_ts, p->kr_hs, p->n_kv_heads, p->kr_cap},
+                {"v_raw", p->vr_bs, p->vr_ts, p->vr_hs, p->n_kv_heads, p->vr_cap},
+                {"q_out", p->qo_bs, p->qo_ts, p->qo_hs, p->n_heads, p->qo_cap}};
+    for (const auto &r : rows)
+        if (!extent(&need, {{p->batch, r.bs}, {p->max_tokens, r.ts}, {r.heads, r.hs}}, p->head_dim) || need > r.cap)
+            return fail("attn_paged_prepare: %s holds %lld elements, the strides need more %s", r.name,
+                        (long long)r.cap, d);
+    if (p->qk_norm) {
+        if (!extent(&need, {{p->n_heads, p->qn_hs}}, p->head_dim) || need > p->qn_cap ||
+            !extent(&need, {{p->n_kv_heads, p->kn_hs}}, p->head_dim) || need > p->kn_cap)
+            return fail("attn_paged_prepare: norm weights hold too few elements %s", d);
+    }
+    if (!extent(&need, {{p->num_pages, p->kv_page_stride}, {p->page_size, p->kv_token_stride},
+                        {p->n_kv_heads, p->kv_head_stride}},
+                p->head_dim) ||
+        need > p->kv_cap)
+        return fail("attn_paged_prepare: KV pools hold %lld elements, the strides need more %s", (long long)p->kv_cap,
+                    d);
+    const int64_t items = (int64_t)p->batch * p->max_tokens * (p->n_heads + 2 * p->n_kv_heads);
+    if ((items + 3) / 4 > (1ll << 31) - 1) return fail("attn_paged_prepare: grid too large %s", d);
+    return ATTN_OK;
+}
+
 std::string dflash_dump(const dflash_params *p) {
     char buf[256];
     snprintf(buf, sizeof buf,
@@ -368,6 +424,23 @@ int attn_paged_prefill(const attn_paged_prefill_params *p, const float *q, const
     return hip_status(attn::launch_paged_prefill(p, &plan, q, k_pool, v_pool, page_table, query_lens, position_starts,
                                                  o, ws, (hipStream_t)stream),
                       "attn_paged_prefill");
+}
+
+int attn_paged_prepare(const attn_paged_prepare_params *p, const float *q_raw, const float *k_raw, const float *v_raw,
+                       const float *q_norm, const float *k_norm, const int32_t *page_table, const int32_t *query_lens,
+                       const int32_t *position_starts, float *q_out, void *k_pool, void *v_pool, void *stream) {
+    int st = check_prepare(p);
+    if (st != ATTN_OK) return st;
+    if (!q_raw || !k_raw || !v_raw || !page_table || !query_lens || !position_starts || !q_out || !k_pool || !v_pool)
+        return fail("attn_paged_prepare: every buffer must be non-NULL");
+    if (p->qk_norm && (!q_norm || !k_norm)) return fail("attn_paged_prepare: qk_norm needs both norm weight buffers");
+    if (!aligned(q_raw, 4) || !aligned(k_raw, 4) || !aligned(v_raw, 4) || !aligned(q_out, 4) || !aligned(k_pool, 2) ||
+        !aligned(v_pool, 2) || !aligned(page_table, 4) || !aligned(query_lens, 4) || !aligned(position_starts, 4) ||
+        (p->qk_norm && (!aligned(q_norm, 4) || !aligned(k_norm, 4))))
+        return fail("attn_paged_prepare: buffers must be aligned to their element size");
+    return hip_status(attn::launch_paged_prepare(p, q_raw, k_raw, v_raw, q_norm, k_norm, page_table, query_lens,
+                                                 position_starts, q_out, k_pool, v_pool, (hipStream_t)stream),
+                      "attn_paged_prepare");
 }
 
 int dflash_validate(const dflash_params *p) { return check_dflash(p, "dflash_validate"); }

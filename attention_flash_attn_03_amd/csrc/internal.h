@@ -106,6 +106,12 @@ hipError_t launch_dflash_verify(const dflash_params *p, const VerifyPlan *plan, 
                                 const float *cur_k, const float *cur_v, const uint32_t *cache_lengths,
                                 const uint32_t *write_positions, float *o, void *ws, hipStream_t stream);
 
+hipError_t launch_paged_prepare(const attn_paged_prepare_params *p, const float *q_raw, const float *k_raw,
+                                const float *v_raw, const float *q_norm, const float *k_norm,
+                                const int32_t *page_table, const int32_t *query_lens,
+                                const int32_t *position_starts, float *q_out, void *k_pool, void *v_pool,
+                                hipStream_t stream);
+
 hipError_t launch_dflash_pack(const dflash_params *p, const uint16_t *ring_k, const uint16_t *ring_v,
                               const float *cur_q, const float *cur_k, const float *cur_v,
                               const uint32_t *cache_lengths, const uint32_t *write_positions,

@@ -13,7 +13,8 @@ synthetic input resident in HBM:
            32/8 heads, d 128: pack -> mask -> attention over the packed
            buffers, the pack-free verify attention read from the ring in
            place, then commit
-  multi    multi-token paged attention: 16 sequences x 16 new tokens over
+  multi    prepare (Q/K RMS norm, rotary embedding, K/V into the pages) and
+           multi-token paged attention: 16 sequences x 16 new tokens over
            contexts of 1024..8192 tokens in 16-token pages, 32/8 heads, d 128
            (block verify straight from the page table)
 W untimed steps, then K timed steps bracketed by torch.cuda.synchronize().
@@ -189,6 +190,14 @@ def main():
         # K and V rows of every context token, Q and O (f32), the page-table entries, lengths and starts
         multi_bytes = (float(mctx.sum()) * 8 * 128 * 2 * 2 + 2.0 * mc.q.nbytes
                        + 4.0 * float(np.sum(-(-mctx // 16))) + 8.0 * len(mctx))
+        # prepare: raw Q/K/V projections of the new tokens, Q/K norm weights
+        mqr = to_dev(workloads.normal_f32(16 * 16 * 32 * 128, [6, 20]).reshape(16, 16, 32, 128))
+        mkr = to_dev(workloads.normal_f32(16 * 16 * 8 * 128, [6, 21]).reshape(16, 16, 8, 128))
+        mvr = to_dev(workloads.normal_f32(16 * 16 * 8 * 128, [6, 22]).reshape(16, 16, 8, 128))
+        mqn = torch.ones((1, 128), dtype=torch.float32, device=dev)
+        mkn = torch.ones((1, 128), dtype=torch.float32, device=dev)
+        # raw Q/K/V read (f32), prepared Q written (f32), K/V rows written (f16), lengths and starts
+        prep_bytes = (mqr.numel() + mkr.numel() + mvr.numel() + mqr.numel()) * 4.0 + mkr.numel() * 2 * 2.0 + 8.0 * 16
         # 4 * heads * d per (query token, visible key): token i of a sequence sees start + i + 1 keys
         multi_flops = 4.0 * 32 * 128 * float(sum(int(st) * int(n) + int(n) * (int(n) + 1) // 2
                                                  for st, n in zip(mc.position_starts, mc.query_lens)))
@@ -213,6 +222,10 @@ def main():
     def run_verify_fused():
         fa.dflash_verify_attention(vp, ring_k, ring_v, cq, ck, cv, vL, vwp, vfo, scale=vc.scale, workspace=vfws)
 
+    def run_prepare():
+        fa.attn_paged_prepare(mqr, mkr, mvr, mqn, mkn, mpt, mql, mst, mq, mkp, mvp, rope_dim=128, rope_theta=1e4,
+                              rope_interleaved=False, epsilon=1e-6, max_context=mpc.max_context)
+
     def run_multi():
         fa.attn_paged_prefill(mq, mkp, mvp, mpt, mql, mst, mo, scale=mpc.scale, max_context=mpc.max_context,
                               workspace=mws)
@@ -229,7 +242,7 @@ def main():
         rows += [("pack", run_pack), ("mask", run_mask), ("verify_attn", run_verify_attn),
                  ("verify_fused", run_verify_fused), ("commit", run_commit)]
     if "multi" in want:
-        rows.append(("paged_prefill", run_multi))
+        rows += [("prepare", run_prepare), ("paged_prefill", run_multi)]
 
     events = {name: [] for name, _ in rows}
     head_start = [0]  # GPU sleep (cycles) ahead of each timed step
@@ -393,6 +406,11 @@ def main():
     for name in ("verify_attn", "verify_fused"):
         if name in comps:
             comps[name]["tflops"] = verify_attn_flops / (avg_ms[name] * 1e-3) / 1e12
+    if "prepare" in avg_ms:
+        ms = avg_ms["prepare"]
+        comps["prepare"] = {"workload": "16 sequences x 16 new tokens, 32/8 heads, d 128: Q/K RMS norm, rotary "
+                                        "embedding on all 128 features, K/V into 16-token f16 pages",
+                            "ms": ms, "gbps": prep_bytes / (ms * 1e-3) / 1e9, "mbytes": prep_bytes / 1e6}
     if "paged_prefill" in avg_ms:
         ms = avg_ms["paged_prefill"]
         comps["paged_prefill"] = {"workload": "16 sequences x 16 new tokens, contexts 1024..8192, 16-token pages, "

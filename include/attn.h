@@ -173,6 +173,44 @@ int attn_paged_prefill(const attn_paged_prefill_params *p, const float *q, const
                        void *stream);
 
 /* ------------------------------------------------------------------------
+ * Prepare ([paged], the prepare dispatch before attention): for token t <
+ * query_lens[b] of sequence b, at position s = position_starts[b] + t,
+ *  - Q and K heads: RMS norm over the head's head_dim features,
+ *      x / sqrt(mean(x^2) + epsilon) * w   (w: the head's norm weights;
+ *      qn_hs / kn_hs = 0 shares one vector across heads), skipped if
+ *      qk_norm = 0; then rotary embedding of the first rope_dim features,
+ *      pair i rotated by s * rope_theta^(-2i/rope_dim), pairs (2i, 2i+1)
+ *      if rope_interleaved else (i, i + rope_dim/2); the rest pass through;
+ *  - V heads: unchanged;
+ *  - prepared Q -> q_out (F32, ready for attn_paged_prefill), K and V ->
+ *    their pools (F16/BF16, rounded to nearest even) at page
+ *    page_table[b][s / page_size], slot s % page_size (positions at or past
+ *    min(max_context, max_pages_per_seq * page_size) are not written).
+ * Raw projections are F32 [batch, max_tokens, heads, >= head_dim] with
+ * strides (bs, ts, hs); a query head stride of 2*head_dim leaves an output
+ * gate half untouched.  Norm weights are F32.  head_dim 128 or 256;
+ * 0 < rope_dim <= head_dim, rope_dim even ([paged] shape rules).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    int32_t batch, n_heads, n_kv_heads, head_dim, max_tokens;
+    int32_t rope_dim, rope_interleaved, qk_norm;
+    int32_t page_size, max_pages_per_seq, num_pages, max_context;
+    int32_t kv_dtype; /* ATTN_F16 | ATTN_BF16 */
+    float epsilon, rope_theta;
+    int64_t qr_bs, qr_ts, qr_hs, kr_bs, kr_ts, kr_hs, vr_bs, vr_ts, vr_hs;
+    int64_t qo_bs, qo_ts, qo_hs;
+    int64_t qn_hs, kn_hs;
+    int64_t kv_page_stride, kv_token_stride, kv_head_stride;
+    int64_t qr_cap, kr_cap, vr_cap, qo_cap, qn_cap, kn_cap, kv_cap;
+} attn_paged_prepare_params;
+
+int attn_paged_prepare(const attn_paged_prepare_params *p, const float *q_raw, const float *k_raw,
+                       const float *v_raw, const float *q_norm, const float *k_norm,
+                       const int32_t *page_table, const int32_t *query_lens,
+                       const int32_t *position_starts, float *q_out, void *k_pool, void *v_pool,
+                       void *stream);
+
+/* ------------------------------------------------------------------------
  * DFlash2 block verify ([pack]).  Geometry as DFlash2AttentionPackParams with
  * the same rules ([pack], validate): 1 <= lanes <= 4; heads > 0; q_heads a
  * multiple of kv_heads; head_dim 128 or 256; 2 <= rows <= 16; window > rows;

@@ -9,6 +9,7 @@ Functions follow the pages as cited in ``oracle.c``:
   attention        -- O1, batched strided masked GQA (two-pass softmax)
   paged_decode     -- O2, single query over a page table
   paged_prefill    -- O1 over keys gathered through a page table, causal by position
+  paged_prepare    -- per-head RMS norm, rotary embedding, K/V write into the pages
   dflash_pack/mask/commit/mask_rows -- O3..O5 and the mask-rows step
   dflash_verify_attention -- O1 over the outputs of O3 and O4 (the verify step)
   bf16_from_f32    -- round-to-nearest-even f32 -> bf16 bits
@@ -167,6 +168,66 @@ def paged_prefill(q, k_pool, v_pool, page_table, query_lens, position_starts, *,
         mask = np.where(t[None, :] <= st + np.arange(n)[:, None], 0.0, -np.inf)[None, None]
         o[b, :n] = attention(q[b:b + 1, :n], kb, vb, mask, scale=scale, kv_bf16=kv_bf16)[0]
     return o
+
+
+def rms_norm(x, w, eps):
+    """x / sqrt(mean(x^2) + eps) * w over the last axis, in float64."""
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * np.asarray(w, np.float64)
+
+
+def rope(x, position, rope_dim, theta, interleaved):
+    """Rotate pair i of the first rope_dim features by position * theta^(-2i/rope_dim):
+    pairs (2i, 2i+1) if interleaved, else (i, i + rope_dim/2).  float64."""
+    x = np.array(x, np.float64, copy=True)
+    half = rope_dim // 2
+    i = np.arange(half, dtype=np.float64)
+    ang = float(position) * np.power(float(theta), -2.0 * i / rope_dim)
+    c, s = np.cos(ang), np.sin(ang)
+    if interleaved:
+        a, b = x[..., 0:rope_dim:2].copy(), x[..., 1:rope_dim:2].copy()
+        x[..., 0:rope_dim:2] = a * c - b * s
+        x[..., 1:rope_dim:2] = a * s + b * c
+    else:
+        a, b = x[..., :half].copy(), x[..., half:rope_dim].copy()
+        x[..., :half] = a * c - b * s
+        x[..., half:rope_dim] = a * s + b * c
+    return x
+
+
+def paged_prepare(q_raw, k_raw, v_raw, q_norm, k_norm, page_table, query_lens, position_starts, k_pool, v_pool, *,
+                  rope_dim, theta, eps, interleaved, cap, kv_bf16=False):
+    """The prepare step: token t < query_lens[b] at position s = position_starts[b] + t;
+    Q and K heads RMS-normed (weights [heads or 1, D]; None: no norm) then rotated;
+    prepared Q returned (float64 [B, T, H, D], NaN for rows past query_lens); K
+    (rotated) and V (as is) rounded to the pool type and written at page
+    page_table[b, s // P], slot s % P while s < cap.  Returns (q_out, k_pool, v_pool)."""
+    B, T, H, _ = q_raw.shape
+    D = k_pool.shape[-1]
+    P = k_pool.shape[1]
+    kp, vp = np.array(k_pool, copy=True), np.array(v_pool, copy=True)
+    q_out = np.full((B, T, H, D), np.nan)
+
+    def to_pool(x):
+        x32 = np.asarray(x, np.float32)
+        return bf16_from_f32(x32) if kv_bf16 else x32.astype(np.float16)
+
+    for b in range(B):
+        n = min(max(int(query_lens[b]), 0), T)
+        st = max(int(position_starts[b]), 0)
+        for t in range(n):
+            s = st + t
+            q = np.asarray(q_raw[b, t, :, :D], np.float64)
+            k = np.asarray(k_raw[b, t, :, :D], np.float64)
+            if q_norm is not None:
+                q = rms_norm(q, q_norm, eps)
+                k = rms_norm(k, k_norm, eps)
+            q_out[b, t] = rope(q, s, rope_dim, theta, interleaved)
+            if s < cap:
+                page = int(page_table[b, s // P])
+                kp[page, s % P] = to_pool(rope(k, s, rope_dim, theta, interleaved))
+                vp[page, s % P] = to_pool(np.asarray(v_raw[b, t, :, :D], np.float32))
+    return q_out, kp, vp
 
 
 def _c(a, dtype):

@@ -27,7 +27,7 @@ def _header_functions():
 
 def test_exports_every_declared_function(lib):
     names = _header_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(_ffi.SIGNATURES)
@@ -293,4 +293,42 @@ def test_paged_prefill_workspace_and_buffers(lib):
     assert b"workspace" in lib.attn_last_error()
     assert lib.attn_paged_prefill(ctypes.byref(p), fake, fake, fake, None, fake, fake, fake, fake, n.value,
                                   None) == _ffi.ATTN_EINVAL
+
+
+def _prepare(**kw):
+    p = _ffi.PrepareParams()
+    base = dict(batch=2, n_heads=8, n_kv_heads=2, head_dim=128, max_tokens=4, rope_dim=64, rope_interleaved=0,
+                qk_norm=1, page_size=16, max_pages_per_seq=8, num_pages=16, max_context=128, kv_dtype=_ffi.ATTN_F16,
+                epsilon=1e-6, rope_theta=1e4,
+                qr_bs=4 * 8 * 128, qr_ts=8 * 128, qr_hs=128, kr_bs=4 * 2 * 128, kr_ts=2 * 128, kr_hs=128,
+                vr_bs=4 * 2 * 128, vr_ts=2 * 128, vr_hs=128, qo_bs=4 * 8 * 128, qo_ts=8 * 128, qo_hs=128,
+                qn_hs=0, kn_hs=0, kv_page_stride=16 * 2 * 128, kv_token_stride=2 * 128, kv_head_stride=128,
+                qr_cap=2 * 4 * 8 * 128, kr_cap=2 * 4 * 2 * 128, vr_cap=2 * 4 * 2 * 128, qo_cap=2 * 4 * 8 * 128,
+                qn_cap=128, kn_cap=128, kv_cap=16 * 16 * 2 * 128)
+    base.update(kw)
+    for k, v in base.items():
+        setattr(p, k, v)
+    return p
+
+
+@pytest.mark.parametrize("kw,msg", [
+    (dict(rope_dim=0), b"rope_dim"), (dict(rope_dim=130), b"rope_dim"), (dict(rope_dim=63), b"rope_dim"),
+    (dict(head_dim=64), b"head_dim"), (dict(n_kv_heads=3), b"multiple"), (dict(kv_dtype=_ffi.ATTN_F32), b"kv_dtype"),
+    (dict(rope_theta=0.0), b"rope_theta"), (dict(epsilon=-1.0), b"epsilon"), (dict(qr_cap=100), b"q_raw holds"),
+    (dict(qn_hs=128), b"norm weights"), (dict(kv_cap=100), b"KV pools"), (dict(max_tokens=0), b"shape"),
+])
+def test_prepare_rejects_before_launch(lib, kw, msg):
+    fake = 1 << 20  # never dereferenced: the call must fail in host validation
+    p = _prepare(**kw)
+    assert lib.attn_paged_prepare(ctypes.byref(p), *([fake] * 11), None) == _ffi.ATTN_EINVAL
+    assert msg in lib.attn_last_error(), lib.attn_last_error()
+
+
+def test_prepare_needs_norm_weights_when_asked(lib):
+    fake = 1 << 20
+    p = _prepare()
+    args = [fake] * 11
+    args[3] = None  # q_norm
+    assert lib.attn_paged_prepare(ctypes.byref(p), *args, None) == _ffi.ATTN_EINVAL
+    assert b"norm" in lib.attn_last_error()
 
