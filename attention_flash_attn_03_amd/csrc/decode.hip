@@ -35,6 +35,9 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kTok = 32;      // tokens per wave step
+// the (sequence, KV head group) units are laid end to end as 32-token tiles and
+// every workgroup takes this many of them
+constexpr int kDecodeTilesPerWorkgroup = 32;
 constexpr int kPgCap = kDecodeTilesPerWorkgroup * kTok + 2;  // page ids of one piece, any page size
 
 struct DecodeArgs {

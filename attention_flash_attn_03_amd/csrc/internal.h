@@ -42,10 +42,6 @@ hipError_t launch_prefill(const attn_prefill_params *p, const PrefillPlan *plan,
                           const void *k, const void *v, const void *mask, float *o, void *ws,
                           hipStream_t stream);
 
-// Paged decode: the (sequence, KV head group) units are laid end to end as
-// 32-token tiles and every workgroup takes the same number of them.
-constexpr int kDecodeTilesPerWorkgroup = 32;
-
 struct DecodePlan {
     int head_dim, group;              // query heads per KV head
     int heads_per_wg;                 // query heads one workgroup serves
