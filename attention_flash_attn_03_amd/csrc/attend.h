@@ -217,7 +217,7 @@ __device__ __forceinline__ void attend_merge_teams(void *xch, int team, int cw, 
     }
 }
 
-// s_waitcnt vmcnt(n * PER) for n <= 4, the count a compile-time immediate
+// s_waitcnt vmcnt(n * PER) for n <= 6, the count a compile-time immediate
 template <int PER>
 __device__ __forceinline__ void attend_wait_tiles(int n) {
     switch (n) {
@@ -225,7 +225,9 @@ __device__ __forceinline__ void attend_wait_tiles(int n) {
     case 1: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory"); break;
     case 2: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER) : "memory"); break;
     case 3: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(3 * PER) : "memory"); break;
-    default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * PER) : "memory"); break;
+    case 4: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(4 * PER) : "memory"); break;
+    case 5: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(5 * PER) : "memory"); break;
+    default: asm volatile("s_waitcnt vmcnt(%0)" ::"n"(6 * PER) : "memory"); break;
     }
 }
 

@@ -419,8 +419,7 @@ __global__ __launch_bounds__(64 * NWD) void decode_partial_kernel(DecodeArgs a) 
 }
 
 // One wave per (sequence, query head): O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
-// over the pieces of its unit.  Lanes read the (m, l) of 64 pieces at a time;
-// the partials are streamed with coalesced loads, eight pieces in flight.
+// over the pieces of its unit.
 template <int D>
 __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
     constexpr int PER_LANE = D / 64;
@@ -432,50 +431,8 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
     const int64_t u0 = seq_start(a, b) + (int64_t)(head / a.heads_per_wg) * tiles;
     int nsplit = tiles == 0 ? 0 : (int)((u0 + tiles - 1) / a.per - u0 / a.per + 1);
     if (nsplit > a.max_splits) nsplit = a.max_splits;
-    const float2 *ml = a.ml + unit * a.max_splits;
-    const float *part = a.part + unit * a.max_splits * D + lane * PER_LANE;
-
-    float mmax = -INFINITY;
-    for (int s = lane; s < nsplit; s += 64) mmax = fmaxf(mmax, ml[s].x);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, off));
-
-    float o[PER_LANE];
-#pragma unroll
-    for (int i = 0; i < PER_LANE; ++i) o[i] = 0.f;
-    float lsum = 0.f;
-    if (mmax != -INFINITY) {
-        for (int s0 = 0; s0 < nsplit; s0 += 64) {
-            const int s = s0 + lane;
-            const float2 my = s < nsplit ? ml[s] : make_float2(-INFINITY, 0.f);
-            const float w = my.x == -INFINITY ? 0.f : exp2f(my.x - mmax);  // pieces that saw no token weigh 0
-            float lw = w * my.y;
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) lw += __shfl_xor(lw, off);
-            lsum += lw;
-            // every piece below nsplit wrote its partial: load eight at a time
-            const int n = min(64, nsplit - s0);
-            int j = 0;
-            for (; j + 8 <= n; j += 8) {
-                float v[8][PER_LANE];
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-#pragma unroll
-                    for (int i = 0; i < PER_LANE; ++i) v[u][i] = part[(int64_t)(s0 + j + u) * D + i];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const float wj = __shfl(w, j + u);
-#pragma unroll
-                    for (int i = 0; i < PER_LANE; ++i) o[i] = fmaf(wj, v[u][i], o[i]);
-                }
-            }
-            for (; j < n; ++j) {
-                const float wj = __shfl(w, j);
-#pragma unroll
-                for (int i = 0; i < PER_LANE; ++i) o[i] = fmaf(wj, part[(int64_t)(s0 + j) * D + i], o[i]);
-            }
-        }
-    }
+    float o[PER_LANE], lsum;
+    merge_pieces<D>(a.ml + unit * a.max_splits, a.part + unit * a.max_splits * D, nsplit, lane, o, lsum);
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     float *orow = a.o + b * a.o_bs + (int64_t)head * a.o_hs + lane * PER_LANE;
 #pragma unroll

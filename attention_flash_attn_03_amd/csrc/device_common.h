@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 namespace attn {
@@ -71,6 +72,62 @@ __device__ __forceinline__ void lds_ahead_schedule() {
         __builtin_amdgcn_sched_group_barrier(0x100, R, 0);  // LDS reads
     }
     __builtin_amdgcn_sched_group_barrier(0x008, M * A, 0);
+}
+
+// Log-sum-exp merge of nsplit partials of one output row, one wave:
+//   o = sum_s 2^(m_s - M) O_s,  lsum = sum_s 2^(m_s - M) l_s,  M = max_s m_s
+// ml[s] = (m_s, l_s) (m in log2 units, -inf for a piece that saw no key, whose
+// O_s is 0); O_s is part[s*D + d], lane l holding d = l*PER + i.  The (m, l) of
+// the first 64 pieces and the first eight O slices are loaded together, so a row
+// of at most eight pieces costs one memory round trip.
+template <int D>
+__device__ __forceinline__ void merge_pieces(const float2 *ml, const float *part, int nsplit, int lane,
+                                                    float (&o)[D / 64], float &lsum) {
+    constexpr int PER = D / 64;
+    part += lane * PER;
+    const float2 my0 = lane < nsplit ? ml[lane] : make_float2(-INFINITY, 0.f);
+    float v0[8][PER];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) v0[u][i] = u < nsplit ? part[(int64_t)u * D + i] : 0.f;
+    float mmax = my0.x;
+    for (int s = 64 + lane; s < nsplit; s += 64) mmax = fmaxf(mmax, ml[s].x);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, off));
+#pragma unroll
+    for (int i = 0; i < PER; ++i) o[i] = 0.f;
+    lsum = 0.f;
+    if (mmax == -INFINITY) return;  // no piece saw a key
+    for (int s0 = 0; s0 < nsplit; s0 += 64) {
+        const float2 my = s0 == 0 ? my0 : (s0 + lane < nsplit ? ml[s0 + lane] : make_float2(-INFINITY, 0.f));
+        const float w = my.x == -INFINITY ? 0.f : exp2f(my.x - mmax);
+        float lw = w * my.y;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) lw += __shfl_xor(lw, off);
+        lsum += lw;
+        const int n = min(64, nsplit - s0);
+        for (int j = 0; j < n; j += 8) {
+            float v[8][PER];
+            if (s0 == 0 && j == 0) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+#pragma unroll
+                    for (int i = 0; i < PER; ++i) v[u][i] = v0[u][i];
+            } else {
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+#pragma unroll
+                    for (int i = 0; i < PER; ++i) v[u][i] = j + u < n ? part[(int64_t)(s0 + j + u) * D + i] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float wj = __shfl(w, (j + u) & 63);  // zero past n: those slices were loaded as 0
+#pragma unroll
+                for (int i = 0; i < PER; ++i) o[i] = fmaf(wj, v[u][i], o[i]);
+            }
+        }
+    }
 }
 
 }  // namespace attn

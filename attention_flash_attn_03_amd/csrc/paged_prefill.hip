@@ -93,8 +93,15 @@ __device__ bool locate_tile(const MultiArgs &a, int64_t pos, int b0, int64_t bas
     return false;
 }
 
-// Tiles per workgroup: the line spread over `target` workgroups (one round on the
-// chip), within [kMultiMinTilesPerWorkgroup, kMultiMaxTilesPerWorkgroup] (wave-wide).
+// Tiles per workgroup for a line of `total` tiles: spread over `target` workgroups
+// (one round on the chip), within [kMultiMinTilesPerWorkgroup, kMultiMaxTilesPerWorkgroup].
+__device__ __forceinline__ int per_for_line(const MultiArgs &a, int64_t total) {
+    int64_t per = (total + a.target - 1) / a.target;
+    per = per < kMultiMinTilesPerWorkgroup ? kMultiMinTilesPerWorkgroup : per;
+    return (int)(per > kMultiMaxTilesPerWorkgroup ? kMultiMaxTilesPerWorkgroup : per);
+}
+
+// Tiles per workgroup of this call's line (wave-wide).
 __device__ int tiles_per_workgroup(const MultiArgs &a) {
     const int lane = threadIdx.x & 63;
     int64_t total = 0;
@@ -103,9 +110,7 @@ __device__ int tiles_per_workgroup(const MultiArgs &a) {
         const int64_t t = bb < a.batch ? (int64_t)seq_info(a, bb).tiles * a.hgroups : 0;
         total += __shfl(scan_lanes(t, lane), 63);
     }
-    int64_t per = (total + a.target - 1) / a.target;
-    per = per < kMultiMinTilesPerWorkgroup ? kMultiMinTilesPerWorkgroup : per;
-    return (int)(per > kMultiMaxTilesPerWorkgroup ? kMultiMaxTilesPerWorkgroup : per);
+    return per_for_line(a, total);
 }
 
 // Line position of sequence b's first unit (wave-wide).
@@ -302,7 +307,7 @@ __global__ __launch_bounds__(64 * NWV * MultiTiling<D>::TEAMS) void multi_partia
     constexpr int DBLK = D / 16;
     constexpr int TILE = kTK * D;
     static_assert((kTK * (D / 8)) % (64 * TEAMS * NWV) == 0, "tile slots must split evenly over the waves");
-    static_assert(TEAMS * (MultiTiling<D>::NGRP - 1) <= 4 &&
+    static_assert(TEAMS * (MultiTiling<D>::NGRP - 1) <= 6 &&
                       TEAMS * (MultiTiling<D>::NGRP - 1) * 2 * (kTK * (D / 8) / (64 * TEAMS * NWV)) <= 63,
                   "vmcnt immediates");
     static_assert(TEAMS == 1 || NWV * (DBLK * 64 * 16 + 64 * 8) <= NSTAGE * 2 * TILE * 2, "team exchange fits");
@@ -335,6 +340,8 @@ __global__ __launch_bounds__(64 * NWV * MultiTiling<D>::TEAMS) void multi_partia
 
 // One wave per (sequence, token, query head): O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
 // over the pieces of its unit; rows past the sequence's query length are not written.
+// One pass over the sequences gives both the line length (hence the tiles per
+// workgroup) and the sequence's place on the line.
 template <int D>
 __global__ __launch_bounds__(256) void multi_merge_kernel(MultiArgs a) {
     constexpr int PER_LANE = D / 64;
@@ -346,53 +353,21 @@ __global__ __launch_bounds__(256) void multi_merge_kernel(MultiArgs a) {
     const int b = (int)(row / ((int64_t)a.n_heads * a.max_tokens));
     const SeqInfo si = seq_info(a, b);
     if (qi >= si.tokens) return;
+    int64_t total = 0, start = 0;
+    for (int b0 = 0; b0 < a.batch; b0 += 64) {
+        const int bb = b0 + lane;
+        const int64_t t = bb < a.batch ? (int64_t)seq_info(a, bb).tiles * a.hgroups : 0;
+        const int64_t incl = scan_lanes(t, lane);
+        if (b >= b0 && b < b0 + 64) start = total + __shfl(incl - t, b - b0);
+        total += __shfl(incl, 63);
+    }
+    const int per = per_for_line(a, total);
     const int hg = (head / a.group) * a.qgroups + (head % a.group) / a.heads_per_wg;
-    const int per = tiles_per_workgroup(a);
-    const int64_t u0 = seq_start(a, b) + (int64_t)hg * si.tiles;
+    const int64_t u0 = start + (int64_t)hg * si.tiles;
     int nsplit = si.tiles == 0 ? 0 : (int)((u0 + si.tiles - 1) / per - u0 / per + 1);
     if (nsplit > a.max_splits) nsplit = a.max_splits;
-    const float2 *ml = a.ml + row * a.max_splits;
-    const float *part = a.part + row * a.max_splits * D + lane * PER_LANE;
-
-    float mmax = -INFINITY;
-    for (int s = lane; s < nsplit; s += 64) mmax = fmaxf(mmax, ml[s].x);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, off));
-    float o[PER_LANE];
-#pragma unroll
-    for (int i = 0; i < PER_LANE; ++i) o[i] = 0.f;
-    float lsum = 0.f;
-    if (mmax != -INFINITY) {
-        for (int s0 = 0; s0 < nsplit; s0 += 64) {
-            const int s = s0 + lane;
-            const float2 my = s < nsplit ? ml[s] : make_float2(-INFINITY, 0.f);
-            const float w = my.x == -INFINITY ? 0.f : exp2f(my.x - mmax);  // pieces with no visible key weigh 0
-            float lw = w * my.y;
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) lw += __shfl_xor(lw, off);
-            lsum += lw;
-            const int n = min(64, nsplit - s0);
-            int j = 0;
-            for (; j + 8 <= n; j += 8) {
-                float v[8][PER_LANE];
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-#pragma unroll
-                    for (int i = 0; i < PER_LANE; ++i) v[u][i] = part[(int64_t)(s0 + j + u) * D + i];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const float wj = __shfl(w, j + u);
-#pragma unroll
-                    for (int i = 0; i < PER_LANE; ++i) o[i] = fmaf(wj, v[u][i], o[i]);
-                }
-            }
-            for (; j < n; ++j) {
-                const float wj = __shfl(w, j);
-#pragma unroll
-                for (int i = 0; i < PER_LANE; ++i) o[i] = fmaf(wj, part[(int64_t)(s0 + j) * D + i], o[i]);
-            }
-        }
-    }
+    float o[PER_LANE], lsum;
+    merge_pieces<D>(a.ml + row * a.max_splits, a.part + row * a.max_splits * D, nsplit, lane, o, lsum);
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     float *orow = a.o + b * a.o_bs + (int64_t)qi * a.o_ts + (int64_t)head * a.o_hs + lane * PER_LANE;
 #pragma unroll

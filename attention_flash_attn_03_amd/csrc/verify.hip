@@ -180,7 +180,7 @@ __global__ __launch_bounds__(64 * NWV * VerifyTiling<D>::TEAMS) void verify_part
     constexpr int DBLK = D / 16;                     // 16-row blocks of O^T
     constexpr int NLD = TK * (D / 8) / (64 * NW);    // loads per wave per K (or V) tile
     static_assert((TK * (D / 8)) % (64 * NW) == 0, "tile slots must split evenly over the waves");
-    static_assert(TEAMS * (NGRP - 1) <= 4 && TEAMS * (NGRP - 1) * 2 * NLD <= 63, "vmcnt immediates");
+    static_assert(TEAMS * (NGRP - 1) <= 6 && TEAMS * (NGRP - 1) * 2 * NLD <= 63, "vmcnt immediates");
     static_assert(TEAMS == 1 || NWV * (DBLK * 64 * 16 + 64 * 8) <= NSTAGE * 2 * TILE * 2, "team exchange fits the ring");
     __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[NSTAGE * 2 * TILE];  // [stage][K, V]
 
