@@ -74,6 +74,24 @@ __device__ __forceinline__ void lds_ahead_schedule() {
     __builtin_amdgcn_sched_group_barrier(0x008, M * A, 0);
 }
 
+// N steps, each an MFMA group whose operand T is read from LDS: the read of step
+// i + DIST is issued before the MFMAs of step i, with scheduling fences that keep
+// this order, so every operand has its own registers and the wait before step i
+// covers only its own read while DIST more are in flight.
+template <int N, int DIST, typename T, typename Load, typename Use>
+__device__ __forceinline__ void lds_pipeline(Load &&load, Use &&use) {
+    T f[DIST + 1];
+#pragma unroll
+    for (int i = 0; i < DIST && i < N; ++i) f[i] = load(i);
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        if (i + DIST < N) f[(i + DIST) % (DIST + 1)] = load(i + DIST);
+        __builtin_amdgcn_sched_barrier(0);
+        use(i, f[i % (DIST + 1)]);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
 // Log-sum-exp merge of nsplit partials of one output row, one wave:
 //   o = sum_s 2^(m_s - M) O_s,  lsum = sum_s 2^(m_s - M) l_s,  M = max_s m_s
 // ml[s] = (m_s, l_s) (m in log2 units, -inf for a piece that saw no key, whose
@@ -82,7 +100,7 @@ __device__ __forceinline__ void lds_ahead_schedule() {
 // of at most eight pieces costs one memory round trip.
 template <int D>
 __device__ __forceinline__ void merge_pieces(const float2 *ml, const float *part, int nsplit, int lane,
-                                                    float (&o)[D / 64], float &lsum) {
+                                             float (&o)[D / 64], float &lsum) {
     constexpr int PER = D / 64;
     part += lane * PER;
     const float2 my0 = lane < nsplit ? ml[lane] : make_float2(-INFINITY, 0.f);

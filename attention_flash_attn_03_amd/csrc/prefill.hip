@@ -46,6 +46,7 @@ namespace {
 
 constexpr int kTile = 64;               // KV rows per step
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kLdsAhead = 4;            // MFMA operand reads in flight ahead of their MFMA
 
 // O and l are rescaled only when a row's running max grows by more than this
 // many binary orders of magnitude; until then the stale max stays the
@@ -660,20 +661,20 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
         // ---- S^T (BK keys x 32 queries) over this wave's head-dim slice
         float16v s[NB];
 #pragma unroll
-        for (int bb = 0; bb < NB; ++bb) {
+        for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[bb][r] = 0.f;
-            const int krow = bb * 32 + col;
-            const uint16_t *kr = kt_lds + krow * D;
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                const int lch = slice * (DS / 8) + 2 * ks + half;
-                const uint4v kf = *reinterpret_cast<const uint4v *>(kr + 8 * (lch ^ k_swz(krow)));
-                s[bb] = mfma32<BF16>(kf, qf[ks], s[bb]);
-                if constexpr (QSPLIT) s[bb] = mfma32<BF16>(kf, qlo[ks], s[bb]);
-            }
-        }
-        lds_ahead_schedule<NB * KSTEPS, 1, QSPLIT ? 2 : 1, 6>();
+        // step i: k-step i / NB of key block i % NB
+        lds_pipeline<NB * KSTEPS, kLdsAhead, uint4v>(
+            [&](int i) __attribute__((always_inline)) {
+                const int krow = (i % NB) * 32 + col;
+                const int lch = slice * (DS / 8) + 2 * (i / NB) + half;
+                return *reinterpret_cast<const uint4v *>(kt_lds + krow * D + 8 * (lch ^ k_swz(krow)));
+            },
+            [&](int i, const uint4v &kf) __attribute__((always_inline)) {
+                s[i % NB] = mfma32<BF16>(kf, qf[i / NB], s[i % NB]);
+                if constexpr (QSPLIT) s[i % NB] = mfma32<BF16>(kf, qlo[i / NB], s[i % NB]);
+            });
 
         // ---- scale and mask (log2 units); this lane holds keys key0 + 32*bb + 8*(r/4) + 4*half + r%4
         if (use_mask) {
@@ -767,21 +768,18 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
         // A 16-lane group g reads 4 keys x 16 columns per ds_read_b64_tr_b16: lane j of the
         // group points at row kb + j/4, columns c0 + 4*(j%4) .. +3; lane j receives
         // rows kb..kb+3 of column c0 + j.
-#pragma unroll
-        for (int u = 0; u < 2 * NB; ++u) {
-            const int bb = u >> 1, e = u & 1;
-            const int r0 = 32 * bb + 16 * e + v_rsub;      // rows r0 (slots 0..3) and r0 + 8 (slots 4..7)
-            const uint16_t *vr0 = vt_lds + r0 * D + v_inner;
-            const uint16_t *vr1 = vt_lds + (r0 + 8) * D + v_inner;
-            const int sw0 = v_swz(r0), sw1 = v_swz(r0 + 8);
-#pragma unroll
-            for (int db = 0; db < DBLK; ++db) {
-                const int lch = 4 * db + v_lchunk0;
-                const uint4v vf = read_tr16_pair(vr0 + 8 * (lch ^ sw0), vr1 + 8 * (lch ^ sw1));
-                acc_o[db] = mfma32<BF16>(vf, pb[u], acc_o[db]);
-            }
-        }
-        lds_ahead_schedule<2 * NB * DBLK, 2, 1, 6>();
+        // step i: P^T slice u = i / DBLK (key block u / 2, half u % 2) into O block i % DBLK
+        lds_pipeline<2 * NB * DBLK, kLdsAhead, uint4v>(
+            [&](int i) __attribute__((always_inline)) {
+                const int u = i / DBLK;
+                const int r0 = 16 * u + v_rsub;  // rows r0 (slots 0..3) and r0 + 8 (slots 4..7)
+                const int lch = 4 * (i % DBLK) + v_lchunk0;
+                return read_tr16_pair(vt_lds + r0 * D + v_inner + 8 * (lch ^ v_swz(r0)),
+                                      vt_lds + (r0 + 8) * D + v_inner + 8 * (lch ^ v_swz(r0 + 8)));
+            },
+            [&](int i, const uint4v &vf) __attribute__((always_inline)) {
+                acc_o[i % DBLK] = mfma32<BF16>(vf, pb[i / DBLK], acc_o[i % DBLK]);
+            });
         lds_done_barrier();  // every wave is done with this stage's buffers
         buf ^= 1;
         st = nxt;
