@@ -31,7 +31,7 @@ struct PrefillPlan {
     // Paired row blocks (masked calls, no KV split): row blocks p and row_blocks-1-p
     // share two workgroups that split their unskipped tiles evenly.
     int pairing;
-    size_t pair_cnt_offset, pair_cnt_bytes;    // u32 [batch][head_groups][row_blocks/2]
+    size_t pair_cnt_offset, pair_cnt_bytes;    // u32 [batch][head_groups][row_blocks/2][arrivals, ready]
     size_t pair_ml_offset, pair_ml_bytes;      // float2 [pairs][2 sides][slots]
     size_t pair_part_offset, pair_part_bytes;  // f32 [pairs][2 sides][slots][D]
     size_t workspace_bytes;

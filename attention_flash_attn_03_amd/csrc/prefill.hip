@@ -62,7 +62,7 @@ struct PrefillArgs {
     float2 *ml;        // split partials (running max in log2 units, running sum)
     float *pair_part;  // paired row blocks: unnormalised O of each side [pairs][2][slots][D]
     float2 *pair_ml;   // paired row blocks: (m, l) of each side [pairs][2][slots]
-    uint32_t *pair_cnt;  // paired row blocks: sides finished [pairs] (zeroed by the classify pass)
+    uint32_t *pair_cnt;  // paired row blocks: [pairs][arrivals, partial ready] (zeroed by the classify pass)
     int64_t q_bs, q_rs, q_hs, k_bs, k_rs, k_hs, v_bs, v_rs, v_hs, m_bs, m_hs, m_rs, o_bs, o_rs, o_hs;
     int batch, rows, kv_len, n_heads, group;
     int rows_per_wg, heads_per_wg, row_blocks, head_groups, blk_heads;
@@ -454,97 +454,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     const float post_scale = PRESCALE ? 1.f : a.score_scale;
     uint4v qf[KSTEPS];
     uint4v qlo[QSPLIT ? KSTEPS : 1];
-    {
-        char *tile = wave_tile(wave);
-        // rows of the pass go straight into the tile with LDS DMA: instruction `it` fills
-        // 64 consecutive 16-byte slots (QRPI rows); the lane that fills slot j of row tr
-        // fetches chunk j ^ (tr & 15) of that row, so chunk c lands at slot c ^ (tr & 15)
-        auto stage_rows = [&](auto esz_c, int pass) __attribute__((always_inline)) {
-            constexpr int ESZ = decltype(esz_c)::value;
-            constexpr int QCPR = DS * ESZ / 16;       // 16-byte chunks per row
-            constexpr int QRPI = 64 / QCPR;            // rows per load instruction
-            const uint32_t tbase = (uint32_t)(uintptr_t)(lds_void *)tile;
-#pragma unroll 1
-            for (int it = 0; it < WT_ROWS / QRPI; ++it) {
-                const int tr = it * QRPI + lane / QCPR;
-                const int c = (lane % QCPR) ^ (tr & 15);
-                const int sl = qwave * 32 + pass * WT_ROWS + tr;
-                const int rh = h0 + sl / a.rows_per_wg;
-                int rr = rb * a.rows_per_wg + sl % a.rows_per_wg;
-                rr = rr < a.rows ? rr : a.rows - 1;
-                const char *src = reinterpret_cast<const char *>(a.q) +
-                                  (b * a.q_bs + (int64_t)rr * a.q_rs + rh * a.q_hs + slice * DS) * ESZ + c * 16;
-                const uint32_t m0 = __builtin_amdgcn_readfirstlane(tbase + it * 1024);
-                asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory");
-            }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        };
-        const int tr = col % WT_ROWS;
-#pragma unroll
-        for (int pass = 0; pass < 32 / WT_ROWS; ++pass) {
-            if (a.q_bf16) {
-                stage_rows(std::integral_constant<int, 2>{}, pass);
-                if (col / WT_ROWS == pass) {
-#pragma unroll
-                    for (int ks = 0; ks < KSTEPS; ++ks) {
-                        const int cc = 2 * ks + half;
-                        const uint4v raw = *reinterpret_cast<const uint4v *>(tile + tr * (DS * 2) + ((cc ^ (tr & 15)) * 16));
-                        if constexpr (BF16) {
-                            qf[ks] = raw;
-                        } else {
-                            uint4v cv;
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                const float lo = bf16_bits_to_f32((uint16_t)(raw[e] & 0xffffu)) * q_scale;
-                                const float hi = bf16_bits_to_f32((uint16_t)(raw[e] >> 16)) * q_scale;
-                                cv[e] = pack2(to_kv16<false>(lo), to_kv16<false>(hi));
-                            }
-                            qf[ks] = cv;
-                        }
-                    }
-                }
-            } else {
-                stage_rows(std::integral_constant<int, 4>{}, pass);
-                if (col / WT_ROWS == pass) {
-#pragma unroll
-                    for (int ks = 0; ks < KSTEPS; ++ks) {
-                        const int cc = 4 * ks + 2 * half;
-                        const float4v x0 =
-                            *reinterpret_cast<const float4v *>(tile + tr * (DS * 4) + ((cc ^ (tr & 15)) * 16)) * q_scale;
-                        const float4v x1 =
-                            *reinterpret_cast<const float4v *>(tile + tr * (DS * 4) + (((cc + 1) ^ (tr & 15)) * 16)) *
-                            q_scale;
-                        uint4v cv;
-                        cv[0] = pack2(to_kv16<BF16>(x0[0]), to_kv16<BF16>(x0[1]));
-                        cv[1] = pack2(to_kv16<BF16>(x0[2]), to_kv16<BF16>(x0[3]));
-                        cv[2] = pack2(to_kv16<BF16>(x1[0]), to_kv16<BF16>(x1[1]));
-                        cv[3] = pack2(to_kv16<BF16>(x1[2]), to_kv16<BF16>(x1[3]));
-                        qf[ks] = cv;
-                        if constexpr (QSPLIT) {
-                            float rest[8];
-#pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                rest[e] = x0[e] - bf16_bits_to_f32((uint16_t)(cv[e / 2] >> (16 * (e & 1))));
-                                rest[4 + e] = x1[e] - bf16_bits_to_f32((uint16_t)(cv[2 + e / 2] >> (16 * (e & 1))));
-                            }
-                            qlo[ks] = uint4v{pack2(f32_to_bf16_rne(rest[0]), f32_to_bf16_rne(rest[1])),
-                                             pack2(f32_to_bf16_rne(rest[2]), f32_to_bf16_rne(rest[3])),
-                                             pack2(f32_to_bf16_rne(rest[4]), f32_to_bf16_rne(rest[5])),
-                                             pack2(f32_to_bf16_rne(rest[6]), f32_to_bf16_rne(rest[7]))};
-                        }
-                    }
-                }
-            }
-        }
-        if (!row_ok) {
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS; ++ks) {
-                qf[ks] = uint4v{0u, 0u, 0u, 0u};
-                if constexpr (QSPLIT) qlo[ks] = qf[ks];
-            }
-        }
-        __syncthreads();  // every wave has its Q before the first K/V stage overwrites the tiles
-    }
 
     const uint16_t *mrow = nullptr;
     if constexpr (HAS_MASK) {
@@ -633,11 +542,144 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 
     int st = next_stage(st_begin);
     int buf = 0;
-    if (st < st_end) {
-        if (HAS_MASK && slice == 0 && stage_code(st) == TILE_MASKED && mask_in_lds(st)) issue_mask(st, 0);
-        const bool full = st * BK + BK <= a.kv_len;
-        kstream.issue(k_lds, kbase, a.k_rs, st * BK, a.kv_len, wave, full);
-        vstream.issue(v_lds, vbase, a.v_rs, st * BK, a.kv_len, wave, full);
+    auto issue_first_stage = [&]() {
+        if (st < st_end) {
+            if (HAS_MASK && slice == 0 && stage_code(st) == TILE_MASKED && mask_in_lds(st)) issue_mask(st, 0);
+            const bool full = st * BK + BK <= a.kv_len;
+            kstream.issue(k_lds, kbase, a.k_rs, st * BK, a.kv_len, wave, full);
+            vstream.issue(v_lds, vbase, a.v_rs, st * BK, a.kv_len, wave, full);
+        }
+    };
+    if (NS == 1 && !a.q_bf16) {
+        // f32 Q over the whole head dim: each lane reads its query row's fragment straight into
+        // registers, and the first K/V stage is requested before those rows are converted, so
+        // the two share one memory round trip
+        const float *qrow = reinterpret_cast<const float *>(a.q) + b * a.q_bs + (int64_t)row_c * a.q_rs +
+                            (int64_t)head * a.q_hs + 8 * half;
+        float4v qraw[KSTEPS][2];
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            qraw[ks][0] = *reinterpret_cast<const float4v *>(qrow + 16 * ks);
+            qraw[ks][1] = *reinterpret_cast<const float4v *>(qrow + 16 * ks + 4);
+        }
+        issue_first_stage();
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            const float4v x0 = qraw[ks][0] * q_scale;
+            const float4v x1 = qraw[ks][1] * q_scale;
+            uint4v cv;
+            cv[0] = pack2(to_kv16<BF16>(x0[0]), to_kv16<BF16>(x0[1]));
+            cv[1] = pack2(to_kv16<BF16>(x0[2]), to_kv16<BF16>(x0[3]));
+            cv[2] = pack2(to_kv16<BF16>(x1[0]), to_kv16<BF16>(x1[1]));
+            cv[3] = pack2(to_kv16<BF16>(x1[2]), to_kv16<BF16>(x1[3]));
+            qf[ks] = row_ok ? cv : uint4v{0u, 0u, 0u, 0u};
+            if constexpr (QSPLIT) {
+                float rest[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    rest[e] = x0[e] - bf16_bits_to_f32((uint16_t)(cv[e / 2] >> (16 * (e & 1))));
+                    rest[4 + e] = x1[e] - bf16_bits_to_f32((uint16_t)(cv[2 + e / 2] >> (16 * (e & 1))));
+                }
+                const uint4v lo = uint4v{pack2(f32_to_bf16_rne(rest[0]), f32_to_bf16_rne(rest[1])),
+                                         pack2(f32_to_bf16_rne(rest[2]), f32_to_bf16_rne(rest[3])),
+                                         pack2(f32_to_bf16_rne(rest[4]), f32_to_bf16_rne(rest[5])),
+                                         pack2(f32_to_bf16_rne(rest[6]), f32_to_bf16_rne(rest[7]))};
+                qlo[ks] = row_ok ? lo : uint4v{0u, 0u, 0u, 0u};
+            }
+        }
+    } else {
+        {
+            char *tile = wave_tile(wave);
+            // rows of the pass go straight into the tile with LDS DMA: instruction `it` fills
+            // 64 consecutive 16-byte slots (QRPI rows); the lane that fills slot j of row tr
+            // fetches chunk j ^ (tr & 15) of that row, so chunk c lands at slot c ^ (tr & 15)
+            auto stage_rows = [&](auto esz_c, int pass) __attribute__((always_inline)) {
+                constexpr int ESZ = decltype(esz_c)::value;
+                constexpr int QCPR = DS * ESZ / 16;       // 16-byte chunks per row
+                constexpr int QRPI = 64 / QCPR;            // rows per load instruction
+                const uint32_t tbase = (uint32_t)(uintptr_t)(lds_void *)tile;
+    #pragma unroll 1
+                for (int it = 0; it < WT_ROWS / QRPI; ++it) {
+                    const int tr = it * QRPI + lane / QCPR;
+                    const int c = (lane % QCPR) ^ (tr & 15);
+                    const int sl = qwave * 32 + pass * WT_ROWS + tr;
+                    const int rh = h0 + sl / a.rows_per_wg;
+                    int rr = rb * a.rows_per_wg + sl % a.rows_per_wg;
+                    rr = rr < a.rows ? rr : a.rows - 1;
+                    const char *src = reinterpret_cast<const char *>(a.q) +
+                                      (b * a.q_bs + (int64_t)rr * a.q_rs + rh * a.q_hs + slice * DS) * ESZ + c * 16;
+                    const uint32_t m0 = __builtin_amdgcn_readfirstlane(tbase + it * 1024);
+                    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory");
+                }
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            };
+            const int tr = col % WT_ROWS;
+    #pragma unroll
+            for (int pass = 0; pass < 32 / WT_ROWS; ++pass) {
+                if (a.q_bf16) {
+                    stage_rows(std::integral_constant<int, 2>{}, pass);
+                    if (col / WT_ROWS == pass) {
+    #pragma unroll
+                        for (int ks = 0; ks < KSTEPS; ++ks) {
+                            const int cc = 2 * ks + half;
+                            const uint4v raw = *reinterpret_cast<const uint4v *>(tile + tr * (DS * 2) + ((cc ^ (tr & 15)) * 16));
+                            if constexpr (BF16) {
+                                qf[ks] = raw;
+                            } else {
+                                uint4v cv;
+    #pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    const float lo = bf16_bits_to_f32((uint16_t)(raw[e] & 0xffffu)) * q_scale;
+                                    const float hi = bf16_bits_to_f32((uint16_t)(raw[e] >> 16)) * q_scale;
+                                    cv[e] = pack2(to_kv16<false>(lo), to_kv16<false>(hi));
+                                }
+                                qf[ks] = cv;
+                            }
+                        }
+                    }
+                } else {
+                    stage_rows(std::integral_constant<int, 4>{}, pass);
+                    if (col / WT_ROWS == pass) {
+    #pragma unroll
+                        for (int ks = 0; ks < KSTEPS; ++ks) {
+                            const int cc = 4 * ks + 2 * half;
+                            const float4v x0 =
+                                *reinterpret_cast<const float4v *>(tile + tr * (DS * 4) + ((cc ^ (tr & 15)) * 16)) * q_scale;
+                            const float4v x1 =
+                                *reinterpret_cast<const float4v *>(tile + tr * (DS * 4) + (((cc + 1) ^ (tr & 15)) * 16)) *
+                                q_scale;
+                            uint4v cv;
+                            cv[0] = pack2(to_kv16<BF16>(x0[0]), to_kv16<BF16>(x0[1]));
+                            cv[1] = pack2(to_kv16<BF16>(x0[2]), to_kv16<BF16>(x0[3]));
+                            cv[2] = pack2(to_kv16<BF16>(x1[0]), to_kv16<BF16>(x1[1]));
+                            cv[3] = pack2(to_kv16<BF16>(x1[2]), to_kv16<BF16>(x1[3]));
+                            qf[ks] = cv;
+                            if constexpr (QSPLIT) {
+                                float rest[8];
+    #pragma unroll
+                                for (int e = 0; e < 4; ++e) {
+                                    rest[e] = x0[e] - bf16_bits_to_f32((uint16_t)(cv[e / 2] >> (16 * (e & 1))));
+                                    rest[4 + e] = x1[e] - bf16_bits_to_f32((uint16_t)(cv[2 + e / 2] >> (16 * (e & 1))));
+                                }
+                                qlo[ks] = uint4v{pack2(f32_to_bf16_rne(rest[0]), f32_to_bf16_rne(rest[1])),
+                                                 pack2(f32_to_bf16_rne(rest[2]), f32_to_bf16_rne(rest[3])),
+                                                 pack2(f32_to_bf16_rne(rest[4]), f32_to_bf16_rne(rest[5])),
+                                                 pack2(f32_to_bf16_rne(rest[6]), f32_to_bf16_rne(rest[7]))};
+                            }
+                        }
+                    }
+                }
+            }
+            if (!row_ok) {
+    #pragma unroll
+                for (int ks = 0; ks < KSTEPS; ++ks) {
+                    qf[ks] = uint4v{0u, 0u, 0u, 0u};
+                    if constexpr (QSPLIT) qlo[ks] = qf[ks];
+                }
+            }
+            __syncthreads();  // every wave has its Q before the first K/V stage overwrites the tiles
+        }
+        issue_first_stage();
     }
     while (st < st_end) {
         const int code = stage_code(st);
@@ -793,8 +835,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     bool write_final = a.splits == 1;
     if constexpr (HAS_MASK) {
         if (side >= 0) {
-            // one side of a cut row block: publish this side, and if the other side is
-            // already done, merge both
+            // one side of a cut row block.  The side that arrives first publishes its partial
+            // and raises the pair's ready flag; the side that arrives second waits for that
+            // flag (the first side has arrived by then and owes only its stores, so the wait
+            // ends) and merges both into the output.
             // the arrival order is broadcast through the second mask buffer: the next task
             // writes it only after the barrier that starts its first stage
             int *arrival = reinterpret_cast<int *>(m_lds + QW * MI * 64);
@@ -802,34 +846,48 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
             const int64_t pu = ((int64_t)b * a.head_groups + hg) * (a.row_blocks >> 1) + pair;
             // The two sides may run on different XCDs, whose L2 caches are not coherent
             // with each other: the partials are written and read with agent-coherent
-            // (sc1) accesses, and only the arrival counter orders them, so no fence has
-            // to write back or invalidate a whole L2.
+            // (sc1) accesses, and only the ready flag orders them, so no fence has to
+            // write back or invalidate a whole L2.
             constexpr int PBYTES = DBLK * 4 * 64 * 16;  // one wave's partial
-            const __amdgpu_buffer_rsrc_t mine = __builtin_amdgcn_make_buffer_rsrc(
-                a.pair_part + ((pu * 2 + side) * NW + wave) * (PBYTES / 4), 0, PBYTES, kRawBufferFlags);
-#pragma unroll
-            for (int db = 0; db < DBLK; ++db)
-#pragma unroll
-                for (int r4 = 0; r4 < 4; ++r4)
-                    __builtin_amdgcn_raw_buffer_store_b128(
-                        __builtin_bit_cast(uint4v, float4v{acc_o[db][4 * r4], acc_o[db][4 * r4 + 1], acc_o[db][4 * r4 + 2],
-                                                           acc_o[db][4 * r4 + 3]}),
-                        mine, ((db * 4 + r4) * 64 + lane) * 16, 0, kAgentCoherent);
-            if (slice == 0 && half == 0) {
-                __hip_atomic_store(&a.pair_ml[(pu * 2 + side) * slots + slot].x, m_run, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(&a.pair_ml[(pu * 2 + side) * slots + slot].y, l_run, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            }
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial is out
-            __syncthreads();
             if (threadIdx.x == 0)
-                *arrival = (int)__hip_atomic_fetch_add(a.pair_cnt + pu, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                *arrival = (int)__hip_atomic_fetch_add(a.pair_cnt + 2 * pu, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __syncthreads();
-            write_final = *arrival == 1;
+            write_final = *arrival != 0;
+            if (!write_final) {
+                const __amdgpu_buffer_rsrc_t mine = __builtin_amdgcn_make_buffer_rsrc(
+                    a.pair_part + ((pu * 2 + side) * NW + wave) * (PBYTES / 4), 0, PBYTES, kRawBufferFlags);
+#pragma unroll
+                for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+                    for (int r4 = 0; r4 < 4; ++r4)
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            __builtin_bit_cast(uint4v, float4v{acc_o[db][4 * r4], acc_o[db][4 * r4 + 1],
+                                                               acc_o[db][4 * r4 + 2], acc_o[db][4 * r4 + 3]}),
+                            mine, ((db * 4 + r4) * 64 + lane) * 16, 0, kAgentCoherent);
+                if (slice == 0 && half == 0) {
+                    __hip_atomic_store(&a.pair_ml[(pu * 2 + side) * slots + slot].x, m_run, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&a.pair_ml[(pu * 2 + side) * slots + slot].y, l_run, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                }
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial is out
+                __syncthreads();
+                if (threadIdx.x == 0)
+                    __hip_atomic_store(a.pair_cnt + 2 * pu + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            } else {
+                if (threadIdx.x == 0) {
+                    // bounded as well, so that no wave can wait forever
+                    for (int spin = 0; spin < (1 << 22); ++spin) {
+                        if (__hip_atomic_load(a.pair_cnt + 2 * pu + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)
+                            break;
+                        __builtin_amdgcn_s_sleep(2);
+                    }
+                }
+                __syncthreads();
+            }
             if (write_final) {
-                // the other side's partial was complete before its increment, which this
-                // side's increment has observed
+                // the other side's partial was complete before its ready flag, which this
+                // side has observed
                 const int other = 1 - side;
                 const float mo = __hip_atomic_load(&a.pair_ml[(pu * 2 + other) * slots + slot].x, __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT);
@@ -1123,7 +1181,7 @@ int plan_prefill(const attn_prefill_params *p, PrefillPlan *plan) {
         const size_t pairs = (size_t)p->batch * plan->head_groups * (plan->row_blocks / 2);
         const size_t slots = (size_t)plan->rows_per_wg * plan->heads_per_wg;
         plan->pair_cnt_offset = off;
-        plan->pair_cnt_bytes = pairs * sizeof(uint32_t);
+        plan->pair_cnt_bytes = 2 * pairs * sizeof(uint32_t);
         off = align256(off + plan->pair_cnt_bytes);
         plan->pair_ml_offset = off;
         plan->pair_ml_bytes = pairs * 2 * slots * sizeof(float2);

@@ -272,33 +272,35 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    print("bench: warmup", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
+    avg_ms, ms_per_step, wall_ms_per_step = {}, None, None
+    if rows:  # every row but the chunked prefill, which is timed on its own below
+        print("bench: warmup", file=sys.stderr, flush=True)
+        for _ in range(args.warmup):
+            step(False)
+        torch.cuda.synchronize()
+        # size the head start: twice the host's enqueue time of one step, in sleep cycles
+        t_host = time.perf_counter()
         step(False)
-    torch.cuda.synchronize()
-    # size the head start: twice the host's enqueue time of one step, in sleep cycles
-    t_host = time.perf_counter()
-    step(False)
-    t_host = time.perf_counter() - t_host
-    torch.cuda.synchronize()
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    torch.cuda._sleep(1 << 20)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    cycles_per_ms = (1 << 20) / max(c0.elapsed_time(c1), 1e-3)
-    head_start[0] = int(min(2.0 * t_host * 1e3 + 0.2, 20.0) * cycles_per_ms)
-    print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    avg_ms = {name: float(np.mean([a.elapsed_time(b_) for a, b_ in ev])) for name, ev in events.items() if ev}
-    # GPU time of a step: first call's start event to the last call's end event
-    first, last = events[rows[0][0]], events[rows[-1][0]]
-    ms_per_step = float(np.mean([a[0].elapsed_time(z[1]) for a, z in zip(first, last)]))
-    wall_ms_per_step = 1e3 * wall / max(1, args.steps)
+        t_host = time.perf_counter() - t_host
+        torch.cuda.synchronize()
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        torch.cuda._sleep(1 << 20)
+        c1.record(stream)
+        torch.cuda.synchronize()
+        cycles_per_ms = (1 << 20) / max(c0.elapsed_time(c1), 1e-3)
+        head_start[0] = int(min(2.0 * t_host * 1e3 + 0.2, 20.0) * cycles_per_ms)
+        print("bench: timing %d steps" % args.steps, file=sys.stderr, flush=True)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            step(True)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        avg_ms = {name: float(np.mean([a.elapsed_time(b_) for a, b_ in ev])) for name, ev in events.items() if ev}
+        # GPU time of a step: first call's start event to the last call's end event
+        first, last = events[rows[0][0]], events[rows[-1][0]]
+        ms_per_step = float(np.mean([a[0].elapsed_time(z[1]) for a, z in zip(first, last)]))
+        wall_ms_per_step = 1e3 * wall / max(1, args.steps)
 
     # ---------------- chunked prefill at head_dim 512, timed on its own (outside the step)
     chunk = None
