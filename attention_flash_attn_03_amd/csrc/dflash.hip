@@ -80,30 +80,50 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(
     *reinterpret_cast<uint4v *>(packed_v + dst_off) = vval;
 }
 
-// One thread writes 8 consecutive mask elements of the flat [b, h, r, k] array.
+// One thread writes 8 consecutive mask elements of the flat [b, h, r, k] array.  The
+// first element's (lane, head, row, position) is found once, with 32-bit index
+// arithmetic whenever the array has fewer than 2^32 elements (integer division is a
+// long instruction sequence on the GPU, and 64-bit division far longer); the other
+// seven follow by stepping the position and carrying into row, head and lane.
+template <typename IDX>
 __global__ __launch_bounds__(kThreads) void mask_kernel(dflash_params p,
                                                         const uint32_t *__restrict__ cache_lengths,
                                                         uint16_t *__restrict__ mask, uint64_t total) {
     const uint64_t first = ((uint64_t)blockIdx.x * kThreads + threadIdx.x) * 8;
     if (first >= total) return;
+    const IDX f = (IDX)first;
+    const IDX row = f / (IDX)p.packed_len;               // flat (lane, head, row) index
+    uint32_t pos = (uint32_t)(f - row * (IDX)p.packed_len);
+    const IDX bh = row / (IDX)p.rows;
+    uint32_t i = (uint32_t)(row - bh * (IDX)p.rows);
+    uint32_t h = (uint32_t)(bh % (IDX)p.q_heads);
+    uint32_t b = (uint32_t)(bh / (IDX)p.q_heads);
+    auto reach_of = [&](uint32_t bb, uint32_t ii) {
+        const uint32_t length = bb < p.lanes ? cache_lengths[bb] : 0u;
+        const uint32_t window_reach = p.window - 1 - ii;
+        return length < window_reach ? length : window_reach;
+    };
+    uint32_t reach = reach_of(b, i);
     uint16_t vals[8];
-    uint64_t row = first / p.packed_len;
-    uint32_t pos = first % p.packed_len;
+#pragma unroll
     for (int e = 0; e < 8; ++e) {
-        const uint32_t i = row % p.rows;
-        const uint64_t b = row / ((uint64_t)p.q_heads * p.rows);
-        const uint32_t length = b < p.lanes ? cache_lengths[b] : 0u;
-        const uint32_t window_reach = p.window - 1 - i;
-        const uint32_t reach = length < window_reach ? length : window_reach;
         const bool visible = pos < p.rows || (pos - p.rows) < reach;
         vals[e] = visible ? (uint16_t)0x0000 : (uint16_t)0xFF80;
         if (++pos == p.packed_len) {
             pos = 0;
-            ++row;
+            if (++i == p.rows) {
+                i = 0;
+                if (++h == p.q_heads) {
+                    h = 0;
+                    ++b;
+                }
+            }
+            reach = reach_of(b, i);
         }
     }
     if (first + 8 <= total) {
         uint4v out;
+#pragma unroll
         for (int e = 0; e < 4; ++e) out[e] = pack2(vals[2 * e], vals[2 * e + 1]);
         *reinterpret_cast<uint4v *>(mask + first) = out;
     } else {
@@ -167,8 +187,13 @@ hipError_t launch_dflash_pack(const dflash_params *p, const uint16_t *ring_k, co
 hipError_t launch_dflash_mask(const dflash_params *p, const uint32_t *cache_lengths, uint16_t *mask,
                               hipStream_t stream) {
     const uint64_t total = (uint64_t)p->lanes * p->q_heads * p->rows * p->packed_len;
-    hipLaunchKernelGGL(mask_kernel, dim3(blocks_for((total + 7) / 8)), dim3(kThreads), 0, stream, *p,
-                       cache_lengths, mask, total);
+    if (total < ((uint64_t)1 << 32)) {
+        hipLaunchKernelGGL(mask_kernel<uint32_t>, dim3(blocks_for((total + 7) / 8)), dim3(kThreads), 0, stream, *p,
+                           cache_lengths, mask, total);
+    } else {
+        hipLaunchKernelGGL(mask_kernel<uint64_t>, dim3(blocks_for((total + 7) / 8)), dim3(kThreads), 0, stream, *p,
+                           cache_lengths, mask, total);
+    }
     return hipGetLastError();
 }
 

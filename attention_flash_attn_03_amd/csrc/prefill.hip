@@ -987,33 +987,52 @@ __global__ __launch_bounds__(256) void classify_kernel(PrefillArgs a, uint8_t *b
         any_nonzero |= (m16 & 0x7fffu) != 0;
     };
     if (a.mask_dma && key0 + kTile <= a.kv_len) {
-        // 8 lanes per 64-key row, 8 keys (16 bytes) per lane, 8 rows per pass; all the
-        // loads of a wave are independent and go out together
+        // 8 lanes per 64-key row, 8 keys (16 bytes) per lane, 8 rows per load; the 8 loads
+        // of 64 rows are requested before any is looked at (addresses clamped to existing
+        // rows, the copies not counted), so they share one memory round trip
         const int k8 = key0 + 8 * (lane & 7);
-#pragma unroll 8
-        for (int s0 = 0; s0 < slots; s0 += 8) {
-            const int s = s0 + (lane >> 3);
-            const int head = h0 + s / a.rows_per_wg;
-            const int row = rb * a.rows_per_wg + s % a.rows_per_wg;
-            if (s < slots && row < a.rows) {
-                const uint4v raw =
-                    *reinterpret_cast<const uint4v *>(mbase + head * a.m_hs + (int64_t)row * a.m_rs + k8);
+        constexpr int U = 8;
+        for (int s0 = 0; s0 < slots; s0 += 8 * U) {
+            uint4v raw[U];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    see((uint16_t)(raw[e] & 0xffffu));
-                    see((uint16_t)(raw[e] >> 16));
+            for (int u = 0; u < U; ++u) {
+                const int s = min(s0 + 8 * u + (lane >> 3), slots - 1);
+                const int head = h0 + s / a.rows_per_wg;
+                const int row = min(rb * a.rows_per_wg + s % a.rows_per_wg, a.rows - 1);
+                raw[u] = *reinterpret_cast<const uint4v *>(mbase + head * a.m_hs + (int64_t)row * a.m_rs + k8);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int s = s0 + 8 * u + (lane >> 3);
+                if (s < slots && rb * a.rows_per_wg + s % a.rows_per_wg < a.rows) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        see((uint16_t)(raw[u][e] & 0xffffu));
+                        see((uint16_t)(raw[u][e] >> 16));
+                    }
                 }
             }
         }
     } else {
-        // any alignment, or the ragged last tile: one key per lane, rows in turn
+        // any alignment, or the ragged last tile: one key per lane; 32 rows are requested
+        // before any is looked at (clamped to existing rows; the copies are not counted)
         const int key = key0 + lane;
         if (key < a.kv_len) {
-#pragma unroll 4
-            for (int s = 0; s < slots; ++s) {
-                const int head = h0 + s / a.rows_per_wg;
-                const int row = rb * a.rows_per_wg + s % a.rows_per_wg;
-                if (row < a.rows) see(mbase[head * a.m_hs + (int64_t)row * a.m_rs + key]);
+            constexpr int U = 32;
+            for (int s0 = 0; s0 < slots; s0 += U) {
+                uint16_t v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int s = min(s0 + u, slots - 1);
+                    const int head = h0 + s / a.rows_per_wg;
+                    const int row = min(rb * a.rows_per_wg + s % a.rows_per_wg, a.rows - 1);
+                    v[u] = mbase[head * a.m_hs + (int64_t)row * a.m_rs + key];
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int s = s0 + u;
+                    if (s < slots && rb * a.rows_per_wg + s % a.rows_per_wg < a.rows) see(v[u]);
+                }
             }
         }
     }
