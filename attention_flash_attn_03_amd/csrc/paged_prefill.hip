@@ -351,20 +351,27 @@ __global__ __launch_bounds__(256) void multi_merge_kernel(MultiArgs a) {
     const int head = (int)(row % a.n_heads);
     const int qi = (int)((row / a.n_heads) % a.max_tokens);
     const int b = (int)(row / ((int64_t)a.n_heads * a.max_tokens));
-    const SeqInfo si = seq_info(a, b);
-    if (qi >= si.tokens) return;
+    // one pass over the sequences' lengths gives this row's sequence (from its lane of the
+    // pass) and the start of its units on the line: one memory round trip before the merge
     int64_t total = 0, start = 0;
+    int tokens = 0, tiles = 0;
     for (int b0 = 0; b0 < a.batch; b0 += 64) {
         const int bb = b0 + lane;
-        const int64_t t = bb < a.batch ? (int64_t)seq_info(a, bb).tiles * a.hgroups : 0;
+        const SeqInfo sb = bb < a.batch ? seq_info(a, bb) : SeqInfo{0, 0, 0, 0};
+        const int64_t t = (int64_t)sb.tiles * a.hgroups;
         const int64_t incl = scan_lanes(t, lane);
-        if (b >= b0 && b < b0 + 64) start = total + __shfl(incl - t, b - b0);
+        if (b >= b0 && b < b0 + 64) {
+            start = total + __shfl(incl - t, b - b0);
+            tokens = __shfl(sb.tokens, b - b0);
+            tiles = __shfl(sb.tiles, b - b0);
+        }
         total += __shfl(incl, 63);
     }
+    if (qi >= tokens) return;
     const int per = per_for_line(a, total);
     const int hg = (head / a.group) * a.qgroups + (head % a.group) / a.heads_per_wg;
-    const int64_t u0 = start + (int64_t)hg * si.tiles;
-    int nsplit = si.tiles == 0 ? 0 : (int)((u0 + si.tiles - 1) / per - u0 / per + 1);
+    const int64_t u0 = start + (int64_t)hg * tiles;
+    int nsplit = tiles == 0 ? 0 : (int)((u0 + tiles - 1) / per - u0 / per + 1);
     if (nsplit > a.max_splits) nsplit = a.max_splits;
     float o[PER_LANE], lsum;
     merge_pieces<D>(a.ml + row * a.max_splits, a.part + row * a.max_splits * D, nsplit, lane, o, lsum);
