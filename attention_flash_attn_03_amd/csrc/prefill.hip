@@ -1053,19 +1053,37 @@ __global__ __launch_bounds__(256) void combine_kernel(PrefillArgs a) {
     const int64_t unit = t / PER_UNIT;
     const int d4 = t % PER_UNIT;
     if (unit >= units) return;
-    float mmax = -INFINITY;
-    for (int s = 0; s < a.splits; ++s) mmax = fmaxf(mmax, a.ml[s * units + unit].x);
+    // eight splits per pass: their (m, l) and partial rows are all requested before any
+    // is used, and the running max is rescaled pass by pass
+    constexpr int U = 8;
+    float mrun = -INFINITY, l = 0.f;
     float4v acc = {0.f, 0.f, 0.f, 0.f};
-    float l = 0.f;
-    if (mmax != -INFINITY) {
-        for (int s = 0; s < a.splits; ++s) {
-            const float2 ml = a.ml[s * units + unit];
-            if (ml.x == -INFINITY) continue;
-            const float w = exp2f(ml.x - mmax);
-            l += w * ml.y;
-            const float4v x = *reinterpret_cast<const float4v *>(a.part + (s * units + unit) * D + 4 * d4);
-            acc += w * x;
+    for (int s0 = 0; s0 < a.splits; s0 += U) {
+        float2 ml[U];
+        float4v x[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int s = min(s0 + u, a.splits - 1);
+            ml[u] = a.ml[s * units + unit];
+            x[u] = *reinterpret_cast<const float4v *>(a.part + (s * units + unit) * D + 4 * d4);
         }
+        float mx = mrun;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (s0 + u < a.splits) mx = fmaxf(mx, ml[u].x);
+        if (mx == -INFINITY) continue;  // no split so far saw a key
+        const float r = mrun == -INFINITY ? 0.f : exp2f(mrun - mx);
+        acc *= r;
+        l *= r;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (s0 + u < a.splits && ml[u].x != -INFINITY) {
+                const float w = exp2f(ml[u].x - mx);
+                l += w * ml[u].y;
+                acc += w * x[u];
+            }
+        }
+        mrun = mx;
     }
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int row = unit % a.rows;
