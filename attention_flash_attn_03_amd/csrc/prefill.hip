@@ -235,9 +235,13 @@ __device__ __forceinline__ float scale_acc(float x, float f) {
     return x;
 }
 
-// Wait until every vector-memory operation of this wave has landed, then
-// meet the other waves.
-__device__ __forceinline__ void wait_all_barrier() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Wait until every vector-memory operation and every LDS read of this wave has
+// completed, then meet the other waves.  At the start of a stage this is the one
+// barrier of the stage: once every wave is past it, no wave reads the previous
+// stage's buffers any more, so the next stage may be requested into them.
+__device__ __forceinline__ void wait_all_barrier() {
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 __device__ __forceinline__ void lds_done_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // QSPLIT: f32 Q against bf16 K/V.  bf16 keeps 8 significant bits, which
@@ -822,10 +826,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
             [&](int i, const uint4v &vf) __attribute__((always_inline)) {
                 acc_o[i % DBLK] = mfma32<BF16>(vf, pb[i / DBLK], acc_o[i % DBLK]);
             });
-        lds_done_barrier();  // every wave is done with this stage's buffers
         buf ^= 1;
         st = nxt;
     }
+    lds_done_barrier();  // every wave is done with the stage buffers, which the epilogue reuses
 
     // ---- epilogue: this lane holds O^T columns query `col`, rows d = slice*DS + 32*db + 8*(r/4) + 4*half + r%4.
     // Split and pair partials are kept in this fragment order (each store instruction
