@@ -446,8 +446,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     const int row_c = row_ok ? row : a.rows - 1;
 
     // ---- Q fragment: B operand of S^T = K Q^T, k = slice*DS + 16*ks + 8*half + i.
-    // The wave's query rows (its DS columns) are read with one contiguous row segment
-    // per load instruction into its LDS tile, then picked up in fragment order.
+    // f32 Q over the whole head dim goes straight into registers in fragment order (below,
+    // with the first K/V stage); otherwise the wave's query rows (its DS columns) are read
+    // with one contiguous row segment per load instruction into its LDS tile, then picked
+    // up in fragment order.
     // Q is rounded to the K/V type anyway (f16, or a bf16 hi + lo pair), so the score
     // scale and log2(e) are folded in before rounding; only bf16 Q against bf16 K/V is
     // used as given (re-rounding would add error) and its scores are scaled after the
