@@ -200,8 +200,8 @@ __device__ __forceinline__ void issue_kv(const DecodeArgs &a, uint16_t *k_tile, 
         const uint16_t *vsrc = a.v_pool + row_off[i] + 8 * (pch ^ v_swz(row));
         const uint32_t mk = __builtin_amdgcn_readfirstlane(kb + i * 1024);
         const uint32_t mv = __builtin_amdgcn_readfirstlane(vb + i * 1024);
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(mk), "v"(ksrc) : "memory");
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(mv), "v"(vsrc) : "memory");
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(mk), "v"(ksrc) : "memory");
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(mv), "v"(vsrc) : "memory");
     }
 }
 

@@ -157,8 +157,8 @@ __device__ __forceinline__ void issue_tile(const MultiArgs &a, uint16_t *k_tile,
         const uint16_t *vsrc = a.v_pool + off + 8 * (pch ^ attend_v_swz(row));
         const uint32_t mk = __builtin_amdgcn_readfirstlane(kb + (i * NW + wave) * 1024);
         const uint32_t mv = __builtin_amdgcn_readfirstlane(vb + (i * NW + wave) * 1024);
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(mk), "v"(ksrc) : "memory");
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(mv), "v"(vsrc) : "memory");
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(mk), "v"(ksrc) : "memory");
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off nt" ::"s"(mv), "v"(vsrc) : "memory");
     }
 }
 
