@@ -137,6 +137,8 @@ struct MultiTiling {
 
 // Gather the K and V rows of tokens 32*t .. 32*t + 31 (clamped to ctx - 1) of one
 // KV head into an LDS stage through the piece's page ids; the waves split the slots.
+// Nontemporal loads: each K/V row is read once per call (for all query columns of
+// its KV head), from pools larger than the last-level cache.
 template <int D, int NW>
 __device__ __forceinline__ void issue_tile(const MultiArgs &a, uint16_t *k_tile, uint16_t *v_tile, const int *s_pg,
                                            int pg0, int t, int ctx, int64_t head_off, int wave, int lane) {
