@@ -28,6 +28,7 @@ __all__ = [
     "paged_prefill_workspace_bytes", "attn_paged_prepare", "dflash_pack", "dflash_mask",
     "dflash_commit", "dflash_mask_rows", "dflash_validate", "kv_pad", "prefill_params", "decode_params",
     "prefill_workspace_bytes", "decode_workspace_bytes", "dflash_verify_attention", "verify_workspace_bytes",
+    "prefill_status",
 ]
 
 _DTYPES = {torch.float32: _ffi.ATTN_F32, torch.float16: _ffi.ATTN_F16, torch.bfloat16: _ffi.ATTN_BF16}
@@ -51,6 +52,26 @@ def _stream(stream) -> int:
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
     return int(stream)
+
+
+def _scratch(workspace: Optional[torch.Tensor], need: int, device, stream) -> torch.Tensor:
+    """The caller's workspace when it holds `need` bytes, else a new one.  A new one is
+    allocated while the stream the kernels run on is current, so the caching allocator
+    hands its block to no work on another stream before those kernels are done with it."""
+    if workspace is not None and workspace.numel() * workspace.element_size() >= need:
+        return workspace
+    if stream is None:
+        s = torch.cuda.current_stream(device)
+    elif isinstance(stream, torch.cuda.Stream):
+        s = stream
+    else:
+        s = torch.cuda.ExternalStream(int(stream), device=device)
+    with torch.cuda.stream(s):
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+
+
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
 
 
 def kv_pad(kv_len: int) -> int:
@@ -101,15 +122,18 @@ def attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, mask: Option
                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """O = softmax(scale * Q K^T + mask) V into `out` (float32), on the device."""
     p = prefill_params(q, k, v, mask, out, scale=scale, kv_len=kv_len)
-    need = prefill_workspace_bytes(p)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = workspace.data_ptr() if (need and workspace is not None) else None
-    ws_len = workspace.numel() * workspace.element_size() if ws_ptr else 0
+    workspace = _scratch(workspace, prefill_workspace_bytes(p), q.device, stream)
     check(_ffi.lib().attn_prefill(ctypes.byref(p), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                                  None if mask is None else mask.data_ptr(), out.data_ptr(), ws_ptr, ws_len,
-                                  _stream(stream)))
+                                  None if mask is None else mask.data_ptr(), out.data_ptr(), workspace.data_ptr(),
+                                  _nbytes(workspace), _stream(stream)))
     return out
+
+
+def prefill_status(workspace: torch.Tensor) -> tuple:
+    """(error flags, merged row blocks): words 0 and 1 of the status block at the start of
+    a prefill workspace, read once the call that used it has completed."""
+    words = workspace[:8].view(torch.int32).cpu().numpy().view("uint32")
+    return int(words[0]), int(words[1])
 
 
 # --------------------------------------------------------------------------- paged decode
@@ -150,13 +174,10 @@ def attn_paged_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tenso
     p = decode_params(q, k_pool, v_pool, page_table, out, scale=scale, max_context=max_context)
     if context_lens.dtype != torch.int32 or not context_lens.is_contiguous() or context_lens.numel() != q.shape[0]:
         raise ValueError("context_lens must be a contiguous int32 [batch] tensor")
-    need = decode_workspace_bytes(p)
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    workspace = _scratch(workspace, decode_workspace_bytes(p), q.device, stream)
     check(_ffi.lib().attn_paged_decode(ctypes.byref(p), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                                        page_table.data_ptr(), context_lens.data_ptr(), out.data_ptr(),
-                                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                       _stream(stream)))
+                                       workspace.data_ptr(), _nbytes(workspace), _stream(stream)))
     return out
 
 
@@ -205,13 +226,10 @@ def attn_paged_prefill(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tens
     for t, n in ((query_lens, "query_lens"), (position_starts, "position_starts")):
         if t.dtype != torch.int32 or not t.is_contiguous() or t.numel() != q.shape[0]:
             raise ValueError("%s must be a contiguous int32 [batch] tensor" % n)
-    need = paged_prefill_workspace_bytes(p)
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    workspace = _scratch(workspace, paged_prefill_workspace_bytes(p), q.device, stream)
     check(_ffi.lib().attn_paged_prefill(ctypes.byref(p), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                                         page_table.data_ptr(), query_lens.data_ptr(), position_starts.data_ptr(),
-                                        out.data_ptr(), workspace.data_ptr(),
-                                        workspace.numel() * workspace.element_size(), _stream(stream)))
+                                        out.data_ptr(), workspace.data_ptr(), _nbytes(workspace), _stream(stream)))
     return out
 
 
@@ -350,12 +368,10 @@ def dflash_verify_attention(params, ring_k, ring_v, cur_q, cur_k, cur_v, cache_l
         _want(t, (torch.float32,), n)
     _want(cache_lengths, _U32, "cache_lengths")
     _want(write_positions, _U32, "write_positions")
-    need = verify_workspace_bytes(p)
-    if workspace is None or workspace.numel() * workspace.element_size() < need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=out.device)
+    workspace = _scratch(workspace, verify_workspace_bytes(p), out.device, stream)
     check(_ffi.lib().dflash_verify_attention(ctypes.byref(p), float(scale), *[t.data_ptr() for t in bufs],
-                                             workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                             _bytes(bufs), _stream(stream)))
+                                             workspace.data_ptr(), _nbytes(workspace), _bytes(bufs),
+                                             _stream(stream)))
     return out
 
 

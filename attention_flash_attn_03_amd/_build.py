@@ -3,11 +3,14 @@
     python -m attention_flash_attn_03_amd._build
 
 Each csrc/*.hip file is compiled to an object in _build/ (in parallel), then
-linked into attention_flash_attn_03_amd/libattn.so.  Always rebuilds.
+linked into attention_flash_attn_03_amd/libattn.so.  Always rebuilds.  The
+library carries the SHA-256 of the sources it was built from
+(attn_source_sha256), which the loader compares with the sources beside it.
 """
 from __future__ import annotations
 
 import glob
+import hashlib
 import os
 import subprocess
 import sys
@@ -15,6 +18,7 @@ from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "attn.h")
 OBJDIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libattn.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -27,9 +31,24 @@ CFLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
+def source_files() -> list:
+    """Every file libattn.so is compiled from: the HIP sources, their headers and the C ABI header."""
+    return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))) + [HEADER]
+
+
+def source_digest() -> str:
+    """SHA-256 over the names and contents of source_files()."""
+    h = hashlib.sha256()
+    for path in source_files():
+        h.update(os.path.basename(path).encode() + b"\0")
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _compile(src: str, digest: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, '-DATTN_SOURCE_SHA256="%s"' % digest, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in l)
     if res.returncode != 0:
@@ -42,8 +61,9 @@ def _compile(src: str) -> str:
 def build(verbose: bool = True) -> str:
     os.makedirs(OBJDIR, exist_ok=True)
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    digest = source_digest()
     with ThreadPoolExecutor(max(1, min(len(sources), os.cpu_count() or 1))) as ex:
-        objs = list(ex.map(_compile, sources))
+        objs = list(ex.map(lambda src: _compile(src, digest), sources))
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)

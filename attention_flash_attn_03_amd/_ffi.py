@@ -1,7 +1,8 @@
 """ctypes mirror of include/attn.h and loader for the in-tree libattn.so.
 
-Loading fails loudly when the library has not been built: there is no other
-implementation behind the binding.
+Loading fails loudly when the library has not been built, or was built from
+other sources than the ones beside it: there is no other implementation
+behind the binding.
 """
 from __future__ import annotations
 
@@ -14,6 +15,8 @@ LIB_PATH = os.path.join(_HERE, "libattn.so")
 ATTN_OK, ATTN_EINVAL, ATTN_EHIP = 0, 1, 2
 ATTN_NONE, ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2, 3
 ATTN_KV_TILE = 64
+ATTN_PREFILL_STATUS_BYTES = 256
+ATTN_PREFILL_WAIT_EXPIRED = 1
 
 _i32, _i64, _u32, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float
 _vp, _sz = ctypes.c_void_p, ctypes.c_size_t
@@ -70,6 +73,7 @@ class DFlashParams(ctypes.Structure):
 # every function the header declares, with its ctypes signature
 SIGNATURES = {
     "attn_last_error": ([], ctypes.c_char_p),
+    "attn_source_sha256": ([], ctypes.c_char_p),
     "attn_kv_pad": ([_u32], _u32),
     "attn_prefill_workspace_bytes": ([ctypes.POINTER(PrefillParams), ctypes.POINTER(_sz)], ctypes.c_int),
     "attn_prefill": ([ctypes.POINTER(PrefillParams), _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
@@ -114,6 +118,11 @@ def lib() -> ctypes.CDLL:
             fn = getattr(handle, name)
             fn.argtypes = args
             fn.restype = res
+        from . import _build
+        built, here = handle.attn_source_sha256().decode(), _build.source_digest()
+        if built != here:
+            raise ImportError("libattn.so was built from other sources (sha256 %s) than the ones beside it (%s); "
+                              "rebuild with `python -m attention_flash_attn_03_amd._build`" % (built, here))
         _lib = handle
     return _lib
 

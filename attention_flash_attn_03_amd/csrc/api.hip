@@ -12,6 +12,10 @@
 
 #include "internal.h"
 
+#ifndef ATTN_SOURCE_SHA256
+#define ATTN_SOURCE_SHA256 "unknown"
+#endif
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -342,6 +346,8 @@ int check_buffers(const char *who, const Need *needs, int n, const uint64_t *byt
 extern "C" {
 
 const char *attn_last_error(void) { return g_last_error.c_str(); }
+
+const char *attn_source_sha256(void) { return ATTN_SOURCE_SHA256; }
 
 uint32_t attn_kv_pad(uint32_t kv_len) { return (kv_len + ATTN_KV_TILE - 1) / ATTN_KV_TILE * ATTN_KV_TILE; }
 

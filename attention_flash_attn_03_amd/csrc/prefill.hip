@@ -24,10 +24,11 @@
 //    stage j.  Q comes in and O goes out through LDS as whole rows
 //    (coalesced), with the score scale folded into Q where that is exact
 //    enough.
-//  * exp2 with log2(e) folded into the score scale; P is rounded to the K/V
-//    type before P V and the running sum l is taken from the rounded P, so
-//    the rounding cancels in O / l.  O is rescaled only when some lane's
-//    running max moved (lazy rescale).
+//  * exp2 with log2(e) folded into the score scale.  With f16 K/V, P is
+//    rounded to f16 before P V and the running sum l is taken from the
+//    rounded P, so the rounding cancels in O / l; with bf16 K/V, P enters P V
+//    as a hi + lo pair of bf16 (two MFMAs).  O is rescaled only when some
+//    lane's running max moved (lazy rescale).
 //  * Masked calls pair row blocks p and RB-1-p across two workgroups that
 //    split their unskipped stages evenly, whatever the mask shape; the side
 //    that finishes a cut block second merges the two partial results
@@ -54,6 +55,11 @@ constexpr int kLdsAhead = 4;            // MFMA operand reads in flight ahead of
 // unchanged.  Rescales then happen a few times per row instead of per tile.
 constexpr float kRescaleThreshold = 8.f;
 
+// Words of the status block at the start of the workspace (ATTN_PREFILL_STATUS_BYTES).
+constexpr int kStatusWords = ATTN_PREFILL_STATUS_BYTES / 4;
+// Polls of a partner's ready flag before the wait gives up (each poll sleeps ~128 clocks).
+constexpr int kPairWaitPolls = 1 << 22;
+
 struct PrefillArgs {
     const void *q, *k, *v, *mask;
     float *o;
@@ -63,6 +69,7 @@ struct PrefillArgs {
     float *pair_part;  // paired row blocks: unnormalised O of each side [pairs][2][slots][D]
     float2 *pair_ml;   // paired row blocks: (m, l) of each side [pairs][2][slots]
     uint32_t *pair_cnt;  // paired row blocks: [pairs][arrivals, partial ready] (zeroed by the classify pass)
+    uint32_t *status;    // status block: [0] error flags, [1] merged row blocks (zeroed at the start of every call)
     int64_t q_bs, q_rs, q_hs, k_bs, k_rs, k_hs, v_bs, v_rs, v_hs, m_bs, m_hs, m_rs, o_bs, o_rs, o_hs;
     int batch, rows, kv_len, n_heads, group;
     int rows_per_wg, heads_per_wg, row_blocks, head_groups, blk_heads;
@@ -94,19 +101,24 @@ __device__ __forceinline__ uint16_t to_kv16(float x) {
     }
 }
 
-// Two probabilities rounded to the K/V type (v_cvt_pk_{f16,bf16}_f32) and
-// their exact sum as rounded (v_dot2 against (1, 1), fp32 accumulation).
-template <bool BF16>
-__device__ __forceinline__ uint32_t pack_p(float p0, float p1, float &sum) {
-    if constexpr (BF16) {
-        const bhalf2v v = {(__bf16)p0, (__bf16)p1};
-        sum = __builtin_amdgcn_fdot2_f32_bf16(v, bhalf2v{(__bf16)1.f, (__bf16)1.f}, sum, false);
-        return __builtin_bit_cast(uint32_t, v);
-    } else {
-        const half2v v = {(_Float16)p0, (_Float16)p1};
-        sum = __builtin_amdgcn_fdot2(v, half2v{(_Float16)1.f, (_Float16)1.f}, sum, false);
-        return __builtin_bit_cast(uint32_t, v);
-    }
+// Two probabilities rounded to f16 (v_cvt_pk_f16_f32) and their exact sum as
+// rounded (v_dot2 against (1, 1), fp32 accumulation), so that the rounding
+// cancels in O / l.
+__device__ __forceinline__ uint32_t pack_p_f16(float p0, float p1, float &sum) {
+    const half2v v = {(_Float16)p0, (_Float16)p1};
+    sum = __builtin_amdgcn_fdot2(v, half2v{(_Float16)1.f, (_Float16)1.f}, sum, false);
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two probabilities as bf16 hi + lo pairs (about 16 significant bits; one bf16
+// rounding, 2^-9 relative, breaks the error bound for a row that sees only a
+// few keys), and their f32 sum.
+__device__ __forceinline__ void pack_p_bf16(float p0, float p1, uint32_t &hi, uint32_t &lo, float &sum) {
+    const bhalf2v h = {(__bf16)p0, (__bf16)p1};
+    const bhalf2v l = {(__bf16)(p0 - (float)h[0]), (__bf16)(p1 - (float)h[1])};
+    sum += p0 + p1;
+    hi = __builtin_bit_cast(uint32_t, h);
+    lo = __builtin_bit_cast(uint32_t, l);
 }
 
 typedef __attribute__((address_space(3))) short4v lds_short4;
@@ -299,6 +311,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     };
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if constexpr (!HAS_MASK) {
+        // without a mask there is no classify pass and no pairing: only this write touches the status block
+        if (blockIdx.x == 0 && threadIdx.x < kStatusWords) a.status[threadIdx.x] = 0u;
+    }
     const int slice = wave % NS;
     const int qwave = wave / NS;
     const int half = lane >> 5;    // which 8-element k half of an MFMA operand this lane feeds
@@ -790,16 +806,21 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
         const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
         float rowsum = 0.f;
         uint4v pb[2 * NB];  // B operands of O^T += V^T P^T: pb[2*bb + e] holds regs 8e..8e+7 of s[bb]
+        uint4v pl[BF16 ? 2 * NB : 1];  // bf16: the low parts of P
 #pragma unroll
         for (int bb = 0; bb < NB; ++bb)
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
-                uint32_t w[4];
+                uint32_t w[4], wl[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    w[i] = pack_p<BF16>(__builtin_amdgcn_exp2f(s[bb][8 * e + 2 * i] - m_use),
-                                        __builtin_amdgcn_exp2f(s[bb][8 * e + 2 * i + 1] - m_use), rowsum);
+                for (int i = 0; i < 4; ++i) {
+                    const float p0 = __builtin_amdgcn_exp2f(s[bb][8 * e + 2 * i] - m_use);
+                    const float p1 = __builtin_amdgcn_exp2f(s[bb][8 * e + 2 * i + 1] - m_use);
+                    if constexpr (BF16) pack_p_bf16(p0, p1, w[i], wl[i], rowsum);
+                    else w[i] = pack_p_f16(p0, p1, rowsum);
+                }
                 pb[2 * bb + e] = uint4v{w[0], w[1], w[2], w[3]};
+                if constexpr (BF16) pl[2 * bb + e] = uint4v{wl[0], wl[1], wl[2], wl[3]};
             }
         rowsum = sum_with_other_half(rowsum);
         l_run = l_run * alpha + rowsum;
@@ -827,6 +848,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
             },
             [&](int i, const uint4v &vf) __attribute__((always_inline)) {
                 acc_o[i % DBLK] = mfma32<BF16>(vf, pb[i / DBLK], acc_o[i % DBLK]);
+                if constexpr (BF16) acc_o[i % DBLK] = mfma32<BF16>(vf, pl[i / DBLK], acc_o[i % DBLK]);
             });
         buf ^= 1;
         st = nxt;
@@ -839,6 +861,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     // LDS tile of the wave (the K/V buffers are free now), one contiguous row segment
     // per store instruction.
     bool write_final = a.splits == 1;
+    bool gave_up = false;
     if constexpr (HAS_MASK) {
         if (side >= 0) {
             // one side of a cut row block.  The side that arrives first publishes its partial
@@ -882,16 +905,29 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
                     __hip_atomic_store(a.pair_cnt + 2 * pu + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             } else {
                 if (threadIdx.x == 0) {
-                    // bounded as well, so that no wave can wait forever
-                    for (int spin = 0; spin < (1 << 22); ++spin) {
-                        if (__hip_atomic_load(a.pair_cnt + 2 * pu + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u)
+                    // Bounded as well, so that no wave can wait forever.  If the bound is
+                    // reached the partner's partial is not used: the row block is written as
+                    // NaN and the status block records the expiry, so the failure is loud.
+                    bool seen = false;
+                    for (int spin = 0; spin < kPairWaitPolls; ++spin) {
+                        if (__hip_atomic_load(a.pair_cnt + 2 * pu + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+                            seen = true;
                             break;
+                        }
                         __builtin_amdgcn_s_sleep(2);
                     }
+                    if (seen) {
+                        __hip_atomic_fetch_add(a.status + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    } else {
+                        __hip_atomic_fetch_or(a.status, (uint32_t)ATTN_PREFILL_WAIT_EXPIRED, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+                    }
+                    *arrival = seen ? 1 : 2;
                 }
                 __syncthreads();
+                gave_up = *arrival == 2;
             }
-            if (write_final) {
+            if (write_final && !gave_up) {
                 // the other side's partial was complete before its ready flag, which this
                 // side has observed
                 const int other = 1 - side;
@@ -920,7 +956,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     }
     if (write_final || a.splits > 1) {
         // rows of this wave's 32 x DS tile: final O (normalised), or a split partial
-        const float sc = write_final ? (l_run > 0.f ? 1.f / l_run : 0.f) : 1.f;
+        const float sc = gave_up ? __builtin_nanf("") : write_final ? (l_run > 0.f ? 1.f / l_run : 0.f) : 1.f;
         char *tile = wave_tile(wave);
         if (!write_final && slice == 0 && half == 0 && row_ok) {
             const int64_t unit = (((int64_t)split * a.batch + b) * a.n_heads + head) * a.rows + row;
@@ -966,10 +1002,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 
 // One wave classifies one (query block, 64-key tile): TILE_SKIP when every
 // entry is -inf, TILE_OPEN when every entry is zero, else TILE_MASKED.  The
-// pass also clears the pair counters the attention pass uses.  Only
+// pass also clears the status block and the pair counters the attention pass uses.  Only
 // entries of real rows (< rows) and keys (< kv_len) are read.  Grid:
 // (ceil(kv_tiles / 4), row_blocks, batch * blk_heads), four waves per block.
 __global__ __launch_bounds__(256) void classify_kernel(PrefillArgs a, uint8_t *blk) {
+    if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < kStatusWords) a.status[threadIdx.x] = 0u;
     if (a.n_pair_cnt > 0) {
         // the pair counters of the attention pass start from zero on every call
         const int64_t nthreads = (int64_t)gridDim.x * gridDim.y * gridDim.z * 256;
@@ -1104,8 +1141,13 @@ hipError_t launch_nw(const PrefillArgs &a, const PrefillPlan *plan, hipStream_t 
     const dim3 grid((unsigned)((int64_t)plan->head_groups * plan->row_blocks * a.splits * a.batch));
     if constexpr (BF16) {
         if (!a.q_bf16) {
-            hipLaunchKernelGGL((prefill_kernel<D, NW, true, MASK, true>), grid, dim3(64 * NW), 0, stream, a);
-            return hipGetLastError();
+            // f32 Q against bf16 K/V at head_dim 256 runs two-wave workgroups only (plan_prefill)
+            if constexpr (D == 256 && NW == 4) {
+                return hipErrorInvalidValue;
+            } else {
+                hipLaunchKernelGGL((prefill_kernel<D, NW, true, MASK, true>), grid, dim3(64 * NW), 0, stream, a);
+                return hipGetLastError();
+            }
         }
     }
     hipLaunchKernelGGL((prefill_kernel<D, NW, BF16, MASK, false>), grid, dim3(64 * NW), 0, stream, a);
@@ -1162,8 +1204,11 @@ int plan_prefill(const attn_prefill_params *p, PrefillPlan *plan) {
     plan->slices = D > 256 ? 2 : 1;
     plan->slice_dim = D / plan->slices;
     const int g = p->n_heads / p->n_kv_heads;
-    // 4 waves hold 128 query slots (64 with two head-dim slices); at least 64 slots
-    const int max_slots = plan->slices == 1 ? 128 : 64;
+    // 4 waves hold 128 query slots (64 with two head-dim slices); at least 64 slots.
+    // f32 Q against bf16 K/V at head_dim 256 (Q carried as a hi + lo pair) runs two-wave
+    // workgroups of 64 slots: the four-wave build does not fit the register file.
+    const bool qsplit = p->q_dtype == ATTN_F32 && p->kv_dtype == ATTN_BF16;
+    const int max_slots = (plan->slices == 1 && !(qsplit && D == 256)) ? 128 : 64;
     int rpw = pow2_at_least(p->rows < 32 ? p->rows : 32);
     int hpw = 1;  // a power of two, so rows_per_wg * heads_per_wg can reach a multiple of 32
     for (int d = 1; d <= g; d *= 2)
@@ -1197,15 +1242,16 @@ int plan_prefill(const attn_prefill_params *p, PrefillPlan *plan) {
     plan->tiles_per_split = (plan->kv_tiles + splits - 1) / splits;
     plan->splits = plan->tiles_per_split > 0 ? (plan->kv_tiles + plan->tiles_per_split - 1) / plan->tiles_per_split : 1;
     if (plan->splits < 1) plan->splits = 1;
-    size_t off = 0;
+    plan->status_offset = 0;
+    size_t off = ATTN_PREFILL_STATUS_BYTES;
     if (p->mask_dtype != ATTN_NONE) {
         const int blk_heads = p->m_hs == 0 ? 1 : plan->head_groups;
         plan->blk_bytes = (size_t)p->batch * blk_heads * plan->row_blocks * plan->blk_stride;
     } else {
         plan->blk_bytes = 0;
     }
-    plan->blk_offset = 0;
-    off = align256(plan->blk_bytes);
+    plan->blk_offset = off;
+    off = align256(off + plan->blk_bytes);
     const size_t units = (size_t)p->batch * p->n_heads * p->rows;
     if (plan->splits > 1) {
         plan->ml_offset = off;
@@ -1249,6 +1295,7 @@ hipError_t launch_prefill(const attn_prefill_params *p, const PrefillPlan *plan,
     a.mask = p->mask_dtype == ATTN_NONE ? nullptr : mask;
     a.o = o;
     uint8_t *w = (uint8_t *)ws;
+    a.status = (uint32_t *)(w + plan->status_offset);
     a.blk = plan->blk_bytes ? w + plan->blk_offset : nullptr;
     a.ml = plan->splits > 1 ? (float2 *)(w + plan->ml_offset) : nullptr;
     a.part = plan->splits > 1 ? (float *)(w + plan->part_offset) : nullptr;

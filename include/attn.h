@@ -44,6 +44,10 @@ typedef enum { ATTN_NONE = 0, ATTN_F32 = 1, ATTN_F16 = 2, ATTN_BF16 = 3 } attn_d
 /* Text of the last non-OK return on the calling thread ("" if none). */
 const char *attn_last_error(void);
 
+/* SHA-256 (lowercase hex) of the source files this library was compiled
+ * from, so that a loader can tell a stale build from a current one. */
+const char *attn_source_sha256(void);
+
 /* KV tile height walked by the kernels: 64 cache rows per step ([prefill],
  * CACHE_ROWS_PER_STEP). */
 #define ATTN_KV_TILE 64
@@ -90,14 +94,29 @@ typedef struct {
     int64_t q_cap, k_cap, v_cap, m_cap, o_cap;
 } attn_prefill_params;
 
-/* Workspace the call needs (tile classification of the mask, and partial
- * results when the KV range is split across workgroups).  Returns ATTN_OK and
- * writes *bytes, or ATTN_EINVAL for parameters attn_prefill would reject. */
+/* Workspace the call needs: a status block, the tile classification of the
+ * mask, and partial results when the KV range or a row block is shared by
+ * workgroups.  At least ATTN_PREFILL_STATUS_BYTES.  Returns ATTN_OK and writes
+ * *bytes, or ATTN_EINVAL for parameters attn_prefill would reject. */
 int attn_prefill_workspace_bytes(const attn_prefill_params *p, size_t *bytes);
+
+/* Status block: the first ATTN_PREFILL_STATUS_BYTES of the workspace, as
+ * uint32 words, cleared by every call before any other of its kernels run
+ * and readable once the call has completed on its stream.
+ *   word 0  error flags.  ATTN_PREFILL_WAIT_EXPIRED: a workgroup that merges
+ *           a row block it shares with another waited for the other's
+ *           partial result past a fixed bound (about 2^22 polls); it wrote
+ *           NaN into that row block's output instead of a wrong value.  The
+ *           other flags are reserved and stay 0.
+ *   word 1  row blocks whose key range two workgroups shared and merged
+ *           (diagnostic: how often that merge ran; 0 for calls without a mask).
+ * The other words are reserved. */
+#define ATTN_PREFILL_STATUS_BYTES 256
+#define ATTN_PREFILL_WAIT_EXPIRED 1u
 
 /* q, k, v, mask: device inputs as described above (mask may be NULL iff
  * mask_dtype == ATTN_NONE); o: device output; ws: device workspace of at
- * least attn_prefill_workspace_bytes() bytes (NULL if that is 0). */
+ * least attn_prefill_workspace_bytes() bytes, 16-byte aligned. */
 int attn_prefill(const attn_prefill_params *p, const void *q, const void *k, const void *v,
                  const void *mask, float *o, void *ws, size_t ws_bytes, void *stream);
 

@@ -5,8 +5,9 @@ KV cache) against the fp64 oracle, elementwise within |err| <= 2e-3 * (1 +
 Covers block verify straight from the page table (16 tokens, 32/8 heads),
 chunks of 64 tokens (MHA), a head_dim 256 group of 3, bf16 pools, odd page
 sizes, sequences with no new tokens (their rows untouched), a fresh prefill
-from position 0, NaN in unused pool slots, strided Q/O, and one token per
-sequence against attn_paged_decode."""
+from position 0, NaN in unused pool slots, strided Q/O, one token per
+sequence against attn_paged_decode, and the same logical KV under two
+physical page placements (bit-identical)."""
 import numpy as np
 import pytest
 import torch
@@ -133,3 +134,20 @@ def test_rejects_too_many_tokens():
     with pytest.raises(fa.AttnError):
         fa.attn_paged_prefill(q, dev(pc.k_pool), dev(pc.v_pool), dev(pc.page_table), dev(mc.query_lens),
                               dev(mc.position_starts), out, scale=pc.scale, max_context=pc.max_context)
+
+
+def test_page_placement_is_invisible(orc):
+    """Two page tables holding the same logical KV in different physical pages give
+    bit-identical output."""
+    from test_gpu_decode import relocate_pages
+    announce("paged prefill same logical KV, two physical page placements")
+    mc = workloads.paged_multi_case(max_tokens=16, batch=5, ctx_lo=40, ctx_hi=3000, num_pages=1100, n_heads=16,
+                                    n_kv_heads=4, head_dim=128, seed=79)
+    a = _run(mc)
+    pc = mc.paged
+    k2, v2, pt2 = relocate_pages(pc, 791)
+    moved_pc = workloads.PagedCase(pc.q, k2, v2, pt2, pc.context_lens, pc.scale, pc.max_context, pc.meta)
+    moved = workloads.PagedMultiCase(moved_pc, mc.q, mc.query_lens, mc.position_starts)
+    b = _run(moved)
+    assert np.array_equal(a, b)
+    _check(a, _oracle(orc, mc), mc, "paged prefill")

@@ -1,11 +1,16 @@
 """GPU parity of attn_prefill against the fp64 oracle, elementwise within
 |err| <= 2e-3 * (1 + |ref|).
 
-Oracle-sized cases span several 64-key tiles with ragged query and key tails;
-the full-size prefill configurations run in the launch configuration the
-benchmark times and are checked on sampled query rows.  Edge cases: fully
-masked rows, padded vs unpadded KV, per-head bf16 masks with the KV range
-split across workgroups, bf16 Q/K/V, no mask, strided views, GQA mapping."""
+Oracle-sized cases span several 64-key tiles with ragged query and key tails,
+including causal shapes whose launch shares the heaviest row blocks between
+two workgroups (the merge of their partial results is counted in the status
+block and must have run).  The full-size prefill configurations run in the
+launch configuration the benchmark times: every query row of the causal 2k
+case, and rows of every row block of the chunked d 512 cases.  Edge cases:
+fully masked rows, padded vs unpadded KV, per-head bf16 masks with the KV
+range split across workgroups, bf16 Q/K/V, f32 Q with bf16 K/V at head_dim
+128/256/512 with f16, bf16 or no mask, strided views, GQA mapping.  Every
+call's status block must show no expired wait."""
 import math
 
 import numpy as np
@@ -19,16 +24,26 @@ from gpu_util import announce, assert_close, dev
 pytestmark = pytest.mark.gpu
 
 
-def _run(case, kv_len=None, mask=True):
+def _call(case, kv_len=None, mask=True):
+    """One attn_prefill call; returns (O, row blocks merged across workgroups)."""
     bf = case.kv_dtype == "bf16"
     q = dev(case.q, case.q_dtype == "bf16")
     k, v = dev(case.k, bf), dev(case.v, bf)
     m = dev(case.mask, case.mask_dtype == "bf16") if (mask and case.mask is not None) else None
     B, R, H, D = case.q.shape
     out = torch.full((B, R, H, D), float("nan"), dtype=torch.float32, device="cuda")
-    fa.attn_prefill(q, k, v, m, out, scale=case.scale, kv_len=kv_len if kv_len is not None else case.kv_len)
+    kv = kv_len if kv_len is not None else case.kv_len
+    p = fa.prefill_params(q, k, v, m, out, scale=case.scale, kv_len=kv)
+    ws = torch.full((fa.prefill_workspace_bytes(p),), 0xA5, dtype=torch.uint8, device="cuda")
+    fa.attn_prefill(q, k, v, m, out, scale=case.scale, kv_len=kv, workspace=ws)
     torch.cuda.synchronize()
-    return out.cpu().numpy()
+    flags, merged = fa.prefill_status(ws)
+    assert flags == 0, "status block flags 0x%x after the call" % flags
+    return out.cpu().numpy(), merged
+
+
+def _run(case, kv_len=None, mask=True):
+    return _call(case, kv_len, mask)[0]
 
 
 def _oracle(orc, case, rows=None, kv_len=None, mask=True):
@@ -61,6 +76,57 @@ def test_prefill_oracle_sized(orc, rows, kv_len, cached, h, hk, d, holes, seed):
                                        head_dim=d, seed=seed, q_std=1 / math.sqrt(d), kv_std=1.0, holes=holes,
                                        scale=1.0)
     assert_close(_run(case), _oracle(orc, case), "prefill")
+
+
+@pytest.mark.parametrize("rows,h,hk,d,batch,kv_dtype", [
+    (192, 2, 1, 128, 1, "f16"),    # three row blocks: the heavy one is shared, the middle one is alone
+    (192, 2, 1, 256, 1, "f16"),
+    (512, 32, 16, 128, 2, "f16"),  # 256 workgroups, every pair shared
+    (512, 16, 8, 512, 2, "f16"),   # head_dim 512 (two head-dim slices), 256 workgroups
+    (192, 2, 1, 128, 1, "bf16"),   # f32 Q + bf16 K/V; the first rows see one to a few keys
+    (1024, 16, 8, 256, 1, "bf16"),  # two-wave workgroups: 256 of them
+    (512, 16, 8, 512, 2, "bf16"),
+])
+def test_prefill_shared_row_blocks(orc, rows, h, hk, d, batch, kv_dtype):
+    """Causal shapes whose launch pairs heavy and light row blocks and cuts the
+    heavy one between the two workgroups; every row against the oracle."""
+    announce("prefill shared row blocks rows=%d h=%d/%d d=%d batch=%d %s" % (rows, h, hk, d, batch, kv_dtype))
+    case = workloads.prefill_synthetic("t", rows=rows, kv_len=rows, cached=0, n_heads=h, n_kv_heads=hk,
+                                       head_dim=d, seed=40 + d + rows, q_std=1 / math.sqrt(d), kv_std=1.0,
+                                       batch=batch, scale=1.0, kv_dtype=kv_dtype)
+    got, merged = _call(case)
+    assert merged > 0, "no row block was shared and merged: the shape does not reach the merge"
+    assert_close(got, _oracle(orc, case), "shared row blocks")
+
+
+@pytest.mark.parametrize("d", [128, 256, 512])
+@pytest.mark.parametrize("mask_dtype", [None, "f16", "bf16"])
+def test_f32_q_bf16_kv(orc, d, mask_dtype):
+    """f32 Q against bf16 K/V (Q carried as a hi + lo bf16 pair), ragged KV tail."""
+    announce("prefill f32 Q + bf16 K/V d=%d mask=%s" % (d, mask_dtype))
+    case = workloads.prefill_synthetic("t", rows=90, kv_len=301, cached=211, n_heads=4, n_kv_heads=2, head_dim=d,
+                                       seed=50 + d, q_std=1 / math.sqrt(d), kv_std=1.0, holes=0.1,
+                                       kv_dtype="bf16", mask_dtype=mask_dtype or "f16", scale=1.0)
+    has_mask = mask_dtype is not None
+    assert_close(_run(case, mask=has_mask), _oracle(orc, case, mask=has_mask), "f32 Q + bf16 K/V")
+
+
+def test_f32_q_bf16_kv_verify_shaped(orc):
+    """f32 Q + bf16 K/V at head_dim 256 with a per-head bf16 mask and few query rows:
+    the two-wave launch with the KV range split across workgroups."""
+    announce("prefill f32 Q + bf16 K/V d=256, per-head bf16 mask, split KV")
+    rng = np.random.Generator(np.random.PCG64(59))
+    b, h, hk, r, kv, d = 2, 4, 2, 16, 777, 256
+    q = (rng.standard_normal((b, r, h, d)) / 16).astype(np.float32)
+    k = workloads.to_bf16_bits(rng.standard_normal((b, kv, hk, d)).astype(np.float32))
+    v = workloads.to_bf16_bits(rng.standard_normal((b, kv, hk, d)).astype(np.float32))
+    mask = np.where(rng.random((b, h, r, kv)) < 0.6, np.float32(0.0), np.float32(-np.inf))
+    mask[:, :, 2, :] = -np.inf
+    case = workloads.PrefillCase("verify256", q, k, v, workloads.to_bf16_bits(mask), 1.0, kv, q_dtype="f32",
+                                 kv_dtype="bf16", mask_dtype="bf16")
+    got = _run(case)
+    assert np.all(got[:, 2] == 0.0)
+    assert_close(got, _oracle(orc, case), "verify-shaped d 256")
 
 
 def test_bf16_kv_no_mask_batched(orc):
@@ -152,20 +218,33 @@ def test_gqa_matches_repeated_kv(orc):
     assert_close(mha, _oracle(orc, rep), "mha")
 
 
-def _sampled_rows(rows, n, seed):
+def _rows_per_block(rows, block, per, seed):
+    """`per` distinct rows from every block of `block` consecutive rows (first and last included)."""
     rng = np.random.Generator(np.random.PCG64(seed))
-    pick = np.unique(np.concatenate([[0, rows - 1], rng.choice(rows, n, replace=False)]))
-    return pick
+    pick = [0, rows - 1]
+    for b0 in range(0, rows, block):
+        n = min(block, rows - b0)
+        pick += list(b0 + rng.choice(n, min(per, n), replace=False))
+    return np.unique(pick)
 
 
-@pytest.mark.parametrize("name,nrows", [("causal2k", 48), ("chunked8k", 12), ("chunked8k_pad", 8)])
-def test_full_size_configs_sampled(orc, name, nrows):
-    announce("prefill full size %s (sampled rows)" % name)
+def test_full_size_causal2k_every_row(orc):
+    announce("prefill full size causal2k, every row")
+    case = workloads.prefill_case("causal2k")
+    got, merged = _call(case)
+    assert merged > 0
+    assert_close(got, _oracle(orc, case), "causal2k")
+
+
+@pytest.mark.parametrize("name,block", [("chunked8k", 16), ("chunked8k_pad", 32)])
+def test_full_size_chunked_every_row_block(orc, name, block):
+    """A row of every `block`-row block (no coarser than the launch's row blocks, so
+    both sides of every shared row block are covered)."""
+    announce("prefill full size %s, a row of every %d-row block" % (name, block))
     case = workloads.prefill_case(name)
-    got = _run(case)
-    rows = _sampled_rows(case.q.shape[1], nrows, 23)
+    got, _ = _call(case)
+    rows = _rows_per_block(case.q.shape[1], block, 1, 23)
     assert_close(got[:, rows], _oracle(orc, case, rows=rows), name)
     if name == "chunked8k_pad":
         unpadded = _run(case, kv_len=8190)
-        padded = _run(case, kv_len=8192)
-        assert_close(padded, unpadded.astype(np.float64), "padded vs unpadded", tol=1e-5)
+        assert_close(got, unpadded.astype(np.float64), "padded vs unpadded", tol=1e-5)

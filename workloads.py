@@ -106,12 +106,13 @@ def prefill_synthetic(name: str, *, rows: int, kv_len: int, cached: int, n_heads
                       n_kv_heads: int, head_dim: int, seed: int, q_std: float, kv_std: float,
                       holes: float = 0.0, batch: int = 1, kv_dtype: str = "f16",
                       kv_rows_alloc: Optional[int] = None, mask_cols: Optional[int] = None,
-                      scale: float = 1.0) -> PrefillCase:
+                      scale: float = 1.0, mask_dtype: str = "f16") -> PrefillCase:
     """Prefill over one contiguous KV range with a frontier (causal) mask.
 
     K/V are laid out [B, KV, HK, D] (row stride HK*D, head stride D).  With
     kv_rows_alloc > kv_len the extra K/V rows are zero and the mask columns
-    past kv_len are -inf (a padded call); mask_cols sets the mask width."""
+    past kv_len are -inf (a padded call); mask_cols sets the mask width.
+    mask_dtype "bf16" stores the same 0/-inf mask as bf16 bit patterns."""
     rng = np.random.Generator(np.random.PCG64(seed))
     kv_alloc = kv_rows_alloc or kv_len
     mcols = mask_cols or kv_alloc
@@ -125,8 +126,10 @@ def prefill_synthetic(name: str, *, rows: int, kv_len: int, cached: int, n_heads
     m, frontier = _frontier_mask(rows, kv_len, cached, holes, rng)
     mask = np.full((batch, 1, rows, mcols), np.float16(-np.inf), np.float16)
     mask[:, 0, :, :kv_len] = m
+    if mask_dtype == "bf16":
+        mask = to_bf16_bits(mask.astype(np.float32))
     return PrefillCase(name, q, _kv_store(kf, kv_dtype), _kv_store(vf, kv_dtype), mask, scale, kv_len,
-                       kv_dtype=kv_dtype, mask_dtype="f16", visible_pairs=frontier * batch,
+                       kv_dtype=kv_dtype, mask_dtype=mask_dtype, visible_pairs=frontier * batch,
                        meta=dict(rows=rows, kv_len=kv_len, n_heads=n_heads, n_kv_heads=n_kv_heads,
                                  head_dim=head_dim, batch=batch, cached=cached, holes=holes))
 
