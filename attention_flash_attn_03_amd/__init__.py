@@ -28,7 +28,7 @@ __all__ = [
     "paged_prefill_workspace_bytes", "attn_paged_prepare", "dflash_pack", "dflash_mask",
     "dflash_commit", "dflash_mask_rows", "dflash_validate", "kv_pad", "prefill_params", "decode_params",
     "prefill_workspace_bytes", "decode_workspace_bytes", "dflash_verify_attention", "verify_workspace_bytes",
-    "prefill_status",
+    "prefill_status", "attn_paged_decode_noalloc",
 ]
 
 _DTYPES = {torch.float32: _ffi.ATTN_F32, torch.float16: _ffi.ATTN_F16, torch.bfloat16: _ffi.ATTN_BF16}
@@ -178,6 +178,20 @@ def attn_paged_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tenso
     check(_ffi.lib().attn_paged_decode(ctypes.byref(p), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                                        page_table.data_ptr(), context_lens.data_ptr(), out.data_ptr(),
                                        workspace.data_ptr(), _nbytes(workspace), _stream(stream)))
+    return out
+
+
+def attn_paged_decode_noalloc(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                              page_table: torch.Tensor, context_lens: torch.Tensor, out: torch.Tensor, *,
+                              scale: float, max_context: int, stream=None) -> torch.Tensor:
+    """attn_paged_decode with the library's static per-GPU scratch array instead of a
+    workspace: allocates nothing.  Calls that overlap in time on one GPU race."""
+    p = decode_params(q, k_pool, v_pool, page_table, out, scale=scale, max_context=max_context)
+    if context_lens.dtype != torch.int32 or not context_lens.is_contiguous() or context_lens.numel() != q.shape[0]:
+        raise ValueError("context_lens must be a contiguous int32 [batch] tensor")
+    check(_ffi.lib().attn_paged_decode_noalloc(ctypes.byref(p), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                               page_table.data_ptr(), context_lens.data_ptr(), out.data_ptr(),
+                                               _stream(stream)))
     return out
 
 

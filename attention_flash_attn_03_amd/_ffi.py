@@ -17,6 +17,7 @@ ATTN_NONE, ATTN_F32, ATTN_F16, ATTN_BF16 = 0, 1, 2, 3
 ATTN_KV_TILE = 64
 ATTN_PREFILL_STATUS_BYTES = 256
 ATTN_PREFILL_WAIT_EXPIRED = 1
+ATTN_DECODE_SCRATCH_BYTES = 64 << 20
 
 _i32, _i64, _u32, _f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_float
 _vp, _sz = ctypes.c_void_p, ctypes.c_size_t
@@ -78,6 +79,7 @@ SIGNATURES = {
     "attn_prefill_workspace_bytes": ([ctypes.POINTER(PrefillParams), ctypes.POINTER(_sz)], ctypes.c_int),
     "attn_prefill": ([ctypes.POINTER(PrefillParams), _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp], ctypes.c_int),
     "attn_paged_decode_workspace_bytes": ([ctypes.POINTER(DecodeParams), ctypes.POINTER(_sz)], ctypes.c_int),
+    "attn_paged_decode_noalloc": ([ctypes.POINTER(DecodeParams), _vp, _vp, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
     "attn_paged_decode": ([ctypes.POINTER(DecodeParams), _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
                           ctypes.c_int),
     "attn_paged_prefill_workspace_bytes": ([ctypes.POINTER(PagedPrefillParams), ctypes.POINTER(_sz)],

@@ -404,6 +404,30 @@ int attn_paged_decode(const attn_decode_params *p, const float *q, const void *k
                       "attn_paged_decode");
 }
 
+int attn_paged_decode_noalloc(const attn_decode_params *p, const float *q, const void *k_pool, const void *v_pool,
+                              const int32_t *page_table, const int32_t *context_lens, float *o, void *stream) {
+    attn::DecodePlan plan;
+    int st = check_decode(p, &plan);
+    if (st != ATTN_OK) return st;
+    if (!q || !k_pool || !v_pool || !page_table || !context_lens || !o)
+        return fail("attn_paged_decode_noalloc: every buffer must be non-NULL");
+    if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(o, 16) ||
+        !aligned(page_table, 4) || !aligned(context_lens, 4))
+        return fail("attn_paged_decode_noalloc: q, pools and out must be 16-byte aligned, tables 4-byte aligned");
+    if (plan.workspace_bytes > ATTN_DECODE_SCRATCH_BYTES)
+        return fail("attn_paged_decode_noalloc: the call needs %zu bytes of scratch, more than the %zu the library "
+                    "holds; use attn_paged_decode with a workspace",
+                    plan.workspace_bytes, (size_t)ATTN_DECODE_SCRATCH_BYTES);
+    void *scratch = nullptr;
+    if (attn::decode_scratch(&scratch) != ATTN_OK) {
+        g_last_error = "attn_paged_decode_noalloc: no scratch address for the current device";
+        return ATTN_EHIP;
+    }
+    return hip_status(attn::launch_paged_decode(p, &plan, q, k_pool, v_pool, page_table, context_lens, o, scratch,
+                                                (hipStream_t)stream),
+                      "attn_paged_decode_noalloc");
+}
+
 int attn_paged_prefill_workspace_bytes(const attn_paged_prefill_params *p, size_t *bytes) {
     attn::MultiPlan plan;
     int st = check_paged_prefill(p, &plan, "attn_paged_prefill_workspace_bytes");

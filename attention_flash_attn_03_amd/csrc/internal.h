@@ -56,6 +56,8 @@ struct DecodePlan {
 };
 
 int plan_decode(const attn_decode_params *p, DecodePlan *plan);
+// Address of this device's ATTN_DECODE_SCRATCH_BYTES scratch array (looked up once per device).
+int decode_scratch(void **ptr);
 
 // Multi-token paged attention: the decode line with up to 64 query columns
 // (heads x tokens) per workgroup.

@@ -154,6 +154,23 @@ int attn_paged_decode(const attn_decode_params *p, const float *q, const void *k
                       const void *v_pool, const int32_t *page_table, const int32_t *context_lens,
                       float *o, void *ws, size_t ws_bytes, void *stream);
 
+/* Paged decode without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Arguments and results are attn_paged_decode's; the
+ * split partials live instead in a static device array of
+ * ATTN_DECODE_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  The call allocates and frees nothing.  It returns
+ * ATTN_EINVAL, enqueueing nothing, when attn_paged_decode_workspace_bytes for
+ * the same parameters exceeds ATTN_DECODE_SCRATCH_BYTES (the paged workload of
+ * 64 sequences of up to 16384 tokens, 32 heads, head_dim 128, needs 34.6 MB),
+ * and ATTN_EHIP if the array's address cannot be found for the current device.
+ * Every call on one GPU shares that GPU's array: calls that may run at the
+ * same time on one GPU (unordered streams) race and give wrong results. */
+#define ATTN_DECODE_SCRATCH_BYTES (64u << 20)
+int attn_paged_decode_noalloc(const attn_decode_params *p, const float *q, const void *k_pool,
+                              const void *v_pool, const int32_t *page_table,
+                              const int32_t *context_lens, float *o, void *stream);
+
 /* ------------------------------------------------------------------------
  * Multi-token paged attention ([paged]: `tokens` new tokens from
  * `position_start`, causal, over the same paged KV layout as decode; the
