@@ -138,8 +138,6 @@ __device__ __forceinline__ uint4v read_tr16_pair(const uint16_t *p0, const uint1
 //  V: logical chunk c of row r sits at physical chunk c ^ 4*(r % 4); the
 //     transposing read (4 consecutive rows x 4 chunks per 32 lanes) hits 16
 //     distinct bank groups.
-__device__ __forceinline__ int k_swz(int row) { return row & 15; }
-__device__ __forceinline__ int v_swz(int row) { return (row & 3) << 2; }
 
 // Row strides (elements) below this keep every offset inside a 64-row stage under 2^32 bytes.
 constexpr int64_t kOff32Stride = (int64_t)1 << 25;
@@ -301,11 +299,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 
     // A WT_ROWS x DS f32 tile per wave for staging rows of O out (and Q in), carved
     // from the K and V buffers (free before the first stage and after the last): half
-    // the waves in each.  32 rows at once where they fit, else 16 in two passes.
+    // the waves in each.
     constexpr int WT_PER = NW / 2 > 0 ? NW / 2 : 1;  // wave tiles per buffer
-    constexpr int WT_ROWS = (2 * BK * D * 2) / (WT_PER * DS * 4) >= 32 ? 32 : 16;
+    constexpr int WT_ROWS = 32;
     constexpr int WT_BYTES = WT_ROWS * DS * 4;
-    static_assert(WT_PER * WT_BYTES <= 2 * BK * D * 2, "staging tiles fit the K/V buffers");
+    // Every launch shape stages its 32 rows in one pass.  (Staging in two passes of 16
+    // rows gave wrong rows in the masked builds that used it, with a cause not found;
+    // that shape is not built.)
+    static_assert(WT_PER * WT_BYTES <= 2 * BK * D * 2, "staging tiles of 32 rows fit the K/V buffers");
     auto wave_tile = [&](int w) -> char * {
         return (w < WT_PER ? reinterpret_cast<char *>(k_lds) : reinterpret_cast<char *>(v_lds)) + (w % WT_PER) * WT_BYTES;
     };
@@ -555,12 +556,32 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     kstream.init(lane, wave, a.k_rs);
     vstream.init(lane, wave, a.v_rs);
 
-    // per-lane pieces of the transposing V read: row kb + j/4, logical chunk
-    // 4*db + 2*(g&1) + (j&3)/2 (plus the slice), element 4*(j&1) inside the chunk
-    const int g16 = lane >> 4, j16 = lane & 15;
-    const int v_rsub = 4 * (g16 >> 1) + (j16 >> 2);
-    const int v_lchunk0 = slice * (DS / 8) + 2 * (g16 & 1) + ((j16 & 3) >> 1);
-    const int v_inner = 4 * (j16 & 1);
+    // LDS byte offsets of the MFMA operand reads.  The swizzles permute only the low
+    // bits of a chunk index, so every read is one of a few lane offsets plus a
+    // compile-time immediate (the ds_read offset field), and no per-step address
+    // has to be held in a register.
+    //  K (A operand of S^T): k-step ks of key block bb reads row 32*bb + col, logical
+    //    chunk slice*DS/8 + 2*ks + half, stored at chunk ^ (col & 15).  For ks = 8*g + r
+    //    that is chunk 16*g + ((2r + half) ^ (col & 15)) past the slice: k_off[r] + g*256
+    //    + bb*32*D*2.
+    uint32_t k_off[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+        k_off[r] = (uint32_t)((col * D + slice * DS + 8 * ((2 * r + half) ^ (col & 15))) * 2);
+    //  V (transposing reads for the A operand of O^T): lane j of 16-lane group g reads row
+    //    16*u + vr (and vr + 8) with vr = 4*(g/2) + j/4, logical chunk slice*DS/8 + 4*db + l0
+    //    with l0 = 2*(g&1) + (j&3)/2, element 4*(j&1); the chunk is stored at chunk ^ 4*(vr&3),
+    //    i.e. 4*(db ^ (vr&3)) + l0 with only db's low two bits changed: v_off[db&3] +
+    //    64*(db & ~3) + u*32*D (+ 16*D for the rows vr + 8).
+    uint32_t v_off[4];
+    {
+        const int g16 = lane >> 4, j16 = lane & 15;
+        const int vr = 4 * (g16 >> 1) + (j16 >> 2);
+        const int l0 = 2 * (g16 & 1) + ((j16 & 3) >> 1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            v_off[q] = (uint32_t)((vr * D + 4 * (j16 & 1) + 8 * (slice * (DS / 8) + 4 * (q ^ (vr & 3)) + l0)) * 2);
+    }
 
     int st = next_stage(st_begin);
     int buf = 0;
@@ -572,7 +593,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
             vstream.issue(v_lds, vbase, a.v_rs, st * BK, a.kv_len, wave, full);
         }
     };
-    if (NS == 1 && !a.q_bf16) {
+    if (NS == 1 && D <= 256 && !a.q_bf16) {
         // f32 Q over the whole head dim: each lane reads its query row's fragment straight into
         // registers, and the first K/V stage is requested before those rows are converted, so
         // the two share one memory round trip
@@ -618,12 +639,13 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
             auto stage_rows = [&](auto esz_c, int pass) __attribute__((always_inline)) {
                 constexpr int ESZ = decltype(esz_c)::value;
                 constexpr int QCPR = DS * ESZ / 16;       // 16-byte chunks per row
-                constexpr int QRPI = 64 / QCPR;            // rows per load instruction
                 const uint32_t tbase = (uint32_t)(uintptr_t)(lds_void *)tile;
     #pragma unroll 1
-                for (int it = 0; it < WT_ROWS / QRPI; ++it) {
-                    const int tr = it * QRPI + lane / QCPR;
-                    const int c = (lane % QCPR) ^ (tr & 15);
+                for (int it = 0; it < WT_ROWS * QCPR / 64; ++it) {
+                    // instruction `it` fills 16-byte slots it*64 .. it*64+63 of the tile
+                    const int slot_i = it * 64 + lane;
+                    const int tr = slot_i / QCPR;
+                    const int c = (slot_i % QCPR) ^ (tr & 15);
                     const int sl = qwave * 32 + pass * WT_ROWS + tr;
                     const int rh = h0 + sl / a.rows_per_wg;
                     int rr = rb * a.rows_per_wg + sl % a.rows_per_wg;
@@ -636,6 +658,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             };
             const int tr = col % WT_ROWS;
+            // tile rows hold logical chunk c at c ^ (tr & 15): as for the K reads, the chunks a lane
+            // picks up are a few lane offsets plus immediates.  bf16 rows: chunk 2*ks + half;
+            // f32 rows: chunks 4*ks + 2*half + e (e = 0, 1).
+            uint32_t qo[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r)
+                qo[r] = a.q_bf16 ? (uint32_t)(tr * (DS * 2) + (((2 * r + half) ^ (tr & 15)) * 16))
+                                 : (uint32_t)(tr * (DS * 4) + (((4 * (r >> 1) + 2 * half + (r & 1)) ^ (tr & 15)) * 16));
     #pragma unroll
             for (int pass = 0; pass < 32 / WT_ROWS; ++pass) {
                 if (a.q_bf16) {
@@ -643,8 +673,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
                     if (col / WT_ROWS == pass) {
     #pragma unroll
                         for (int ks = 0; ks < KSTEPS; ++ks) {
-                            const int cc = 2 * ks + half;
-                            const uint4v raw = *reinterpret_cast<const uint4v *>(tile + tr * (DS * 2) + ((cc ^ (tr & 15)) * 16));
+                            const uint4v raw = *reinterpret_cast<const uint4v *>(tile + qo[ks & 7] + (ks >> 3) * 256);
                             if constexpr (BF16) {
                                 qf[ks] = raw;
                             } else {
@@ -664,12 +693,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
                     if (col / WT_ROWS == pass) {
     #pragma unroll
                         for (int ks = 0; ks < KSTEPS; ++ks) {
-                            const int cc = 4 * ks + 2 * half;
-                            const float4v x0 =
-                                *reinterpret_cast<const float4v *>(tile + tr * (DS * 4) + ((cc ^ (tr & 15)) * 16)) * q_scale;
-                            const float4v x1 =
-                                *reinterpret_cast<const float4v *>(tile + tr * (DS * 4) + (((cc + 1) ^ (tr & 15)) * 16)) *
-                                q_scale;
+                            const char *row = tile + (ks >> 2) * 256;
+                            const float4v x0 = *reinterpret_cast<const float4v *>(row + qo[2 * (ks & 3)]) * q_scale;
+                            const float4v x1 = *reinterpret_cast<const float4v *>(row + qo[2 * (ks & 3) + 1]) * q_scale;
                             uint4v cv;
                             cv[0] = pack2(to_kv16<BF16>(x0[0]), to_kv16<BF16>(x0[1]));
                             cv[1] = pack2(to_kv16<BF16>(x0[2]), to_kv16<BF16>(x0[3]));
@@ -731,9 +757,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
         // step i: k-step i / NB of key block i % NB
         lds_pipeline<NB * KSTEPS, kLdsAhead, uint4v>(
             [&](int i) __attribute__((always_inline)) {
-                const int krow = (i % NB) * 32 + col;
-                const int lch = slice * (DS / 8) + 2 * (i / NB) + half;
-                return *reinterpret_cast<const uint4v *>(kt_lds + krow * D + 8 * (lch ^ k_swz(krow)));
+                const int bb = i % NB, ks = i / NB;
+                return *reinterpret_cast<const uint4v *>(reinterpret_cast<const char *>(kt_lds) + k_off[ks & 7] +
+                                                         (ks >> 3) * 256 + bb * 32 * D * 2);
             },
             [&](int i, const uint4v &kf) __attribute__((always_inline)) {
                 s[i % NB] = mfma32<BF16>(kf, qf[i / NB], s[i % NB]);
@@ -840,11 +866,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
         // step i: P^T slice u = i / DBLK (key block u / 2, half u % 2) into O block i % DBLK
         lds_pipeline<2 * NB * DBLK, kLdsAhead, uint4v>(
             [&](int i) __attribute__((always_inline)) {
-                const int u = i / DBLK;
-                const int r0 = 16 * u + v_rsub;  // rows r0 (slots 0..3) and r0 + 8 (slots 4..7)
-                const int lch = 4 * (i % DBLK) + v_lchunk0;
-                return read_tr16_pair(vt_lds + r0 * D + v_inner + 8 * (lch ^ v_swz(r0)),
-                                      vt_lds + (r0 + 8) * D + v_inner + 8 * (lch ^ v_swz(r0 + 8)));
+                const int u = i / DBLK, db = i % DBLK;  // rows 16u + vr (slots 0..3) and 16u + vr + 8 (slots 4..7)
+                const char *p0 = reinterpret_cast<const char *>(vt_lds) + v_off[db & 3] + 64 * (db & ~3) + u * 32 * D;
+                return read_tr16_pair(reinterpret_cast<const uint16_t *>(p0),
+                                      reinterpret_cast<const uint16_t *>(p0 + 16 * D));
             },
             [&](int i, const uint4v &vf) __attribute__((always_inline)) {
                 acc_o[i % DBLK] = mfma32<BF16>(vf, pb[i / DBLK], acc_o[i % DBLK]);
@@ -963,12 +988,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
             a.ml[unit] = make_float2(m_run, l_run);
         }
         constexpr int CPR = DS / 4;      // 16-byte chunks per row
-        constexpr int RPI = 64 / CPR;    // rows per store instruction
-        const int c = lane % CPR;
+        // this lane's chunks of its row: 8*db + 2*r4 + half, stored at chunk ^ (tr & 15), i.e.
+        // eo[2*(db&1) ... ] lane offsets plus 256*(db >> 1)
+        const int etr = col % WT_ROWS;
+        uint32_t eo[8];
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+            eo[r] = (uint32_t)(etr * (DS * 4) + (((8 * (r >> 2) + 2 * (r & 3) + half) ^ (etr & 15)) * 16));
 #pragma unroll
         for (int pass = 0; pass < 32 / WT_ROWS; ++pass) {
             if (col / WT_ROWS == pass) {
-                const int tr = col % WT_ROWS;
 #pragma unroll
                 for (int db = 0; db < DBLK; ++db)
 #pragma unroll
@@ -976,13 +1005,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
                         float4v x;
 #pragma unroll
                         for (int e = 0; e < 4; ++e) x[e] = acc_o[db][4 * r4 + e] * sc;
-                        const int cc = 8 * db + 2 * r4 + half;  // 16-byte chunk of the row
-                        *reinterpret_cast<float4v *>(tile + tr * (DS * 4) + ((cc ^ (tr & 15)) * 16)) = x;
+                        *reinterpret_cast<float4v *>(tile + eo[4 * (db & 1) + r4] + (db >> 1) * 256) = x;
                     }
             }
 #pragma unroll
-            for (int it = 0; it < WT_ROWS / RPI; ++it) {
-                const int tr = it * RPI + lane / CPR;
+            for (int it = 0; it < WT_ROWS * CPR / 64; ++it) {
+                // store instruction `it` writes 16-byte chunks it*64 .. it*64+63 of the tile's rows
+                const int tr = (it * 64 + lane) / CPR;
+                const int c = (it * 64 + lane) % CPR;
                 const int sl = qwave * 32 + pass * WT_ROWS + tr;
                 const int rh = h0 + sl / a.rows_per_wg;
                 const int rr = rb * a.rows_per_wg + sl % a.rows_per_wg;
@@ -1201,13 +1231,13 @@ static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 int plan_prefill(const attn_prefill_params *p, PrefillPlan *plan) {
     const int D = p->head_dim;
     plan->head_dim = D;
+    const bool qsplit = p->q_dtype == ATTN_F32 && p->kv_dtype == ATTN_BF16;
     plan->slices = D > 256 ? 2 : 1;
     plan->slice_dim = D / plan->slices;
     const int g = p->n_heads / p->n_kv_heads;
     // 4 waves hold 128 query slots (64 with two head-dim slices); at least 64 slots.
     // f32 Q against bf16 K/V at head_dim 256 (Q carried as a hi + lo pair) runs two-wave
     // workgroups of 64 slots: the four-wave build does not fit the register file.
-    const bool qsplit = p->q_dtype == ATTN_F32 && p->kv_dtype == ATTN_BF16;
     const int max_slots = (plan->slices == 1 && !(qsplit && D == 256)) ? 128 : 64;
     int rpw = pow2_at_least(p->rows < 32 ? p->rows : 32);
     int hpw = 1;  // a power of two, so rows_per_wg * heads_per_wg can reach a multiple of 32
