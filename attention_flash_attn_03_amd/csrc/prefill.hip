@@ -1030,6 +1030,295 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     }  // task
 }
 
+// wide_kernel: head_dim 512 with every wave over the whole head dimension.  Four
+// waves of 32 query slots make a 128-slot workgroup: each K/V byte feeds twice the
+// queries of the two-slice layout and no partial scores are exchanged between
+// waves.  Q (f16, or bf16 against bf16 K/V) lives in 128 VGPRs and O^T in all 256
+// AGPRs, so the kernel keeps no other per-lane array: MFMA operand and mask reads
+// are lane offsets plus immediates, Q is converted eight k-steps at a time, and O
+// leaves straight from the accumulators.  No KV split and no row-block pairing:
+// workgroup i takes the i-th (head group, row block, batch) item with the last row
+// blocks (the heaviest under a causal frontier) dispatched first, so the hardware's
+// in-order dispatch balances the tail.
+template <int D, bool BF16, int MASK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void wide_kernel(PrefillArgs a) {
+    constexpr int NW = 4;
+    constexpr bool HAS_MASK = MASK != 0;
+    constexpr bool MBF16 = MASK == 2;
+    constexpr int KSTEPS = D / 16;
+    constexpr int DBLK = D / 32;
+    constexpr int BK = 32;                     // keys per stage: two stages of K and V are 128 KB
+    constexpr int NB = BK / 32;
+    constexpr int SPT = kTile / BK;
+    constexpr int STAGE_ELEMS = BK * D;
+    constexpr int MI = 2 * NB;                 // mask DMA instructions per wave per stage
+    using KS = TileStream<D, NW, BK, false>;
+    using VS = TileStream<D, NW, BK, true>;
+    __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2 * STAGE_ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2 * STAGE_ELEMS];
+    __shared__ __attribute__((aligned(1024))) uint4v m_lds[HAS_MASK ? 2 * NW * MI * 64 : 1];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int half = lane >> 5;
+    const int col = lane & 31;
+    if constexpr (!HAS_MASK) {
+        if (blockIdx.x == 0 && threadIdx.x < kStatusWords) a.status[threadIdx.x] = 0u;
+    }
+    int lin = blockIdx.x;
+    const int hg = lin % a.head_groups;
+    lin /= a.head_groups;
+    const int rb = a.row_blocks - 1 - lin % a.row_blocks;
+    const int b = lin / a.row_blocks;
+    const int h0 = hg * a.heads_per_wg;
+    const int kvh = h0 / a.group;
+    const int n_stages = (a.kv_len + BK - 1) / BK;
+
+    const int slot = wave * 32 + col;
+    const int head = h0 + slot / a.rows_per_wg;
+    const int row = rb * a.rows_per_wg + slot % a.rows_per_wg;
+    const bool row_ok = row < a.rows;
+    const int row_c = row_ok ? row : a.rows - 1;
+
+    const_u32 *blk_row = nullptr;
+    if constexpr (HAS_MASK)
+        blk_row = (const_u32 *)(a.blk + (((int64_t)b * a.blk_heads + (a.blk_heads == 1 ? 0 : hg)) * a.row_blocks + rb) *
+                                            a.blk_stride);
+    auto stage_code = [&](int st) -> int {
+        if constexpr (HAS_MASK) {
+            const int t = st / SPT;
+            return (int)((blk_row[t >> 2] >> (8 * (t & 3))) & 0xffu);
+        } else {
+            return TILE_OPEN;
+        }
+    };
+    auto next_stage = [&](int from) {
+        int st = from;
+        while (st < n_stages && stage_code(st) == TILE_SKIP) ++st;
+        return st;
+    };
+    const uint16_t *mrow = nullptr;
+    if constexpr (HAS_MASK) mrow = (const uint16_t *)a.mask + b * a.m_bs + head * a.m_hs + (int64_t)row_c * a.m_rs;
+    auto mask_in_lds = [&](int st) { return a.mask_dma && st * BK + BK <= a.kv_len; };
+    // mask of a stage into this wave's LDS region: instruction i fetches, for each of the
+    // wave's 32 query rows, the 8-key chunks 2i (lanes 0..31) and 2i+1 (lanes 32..63)
+    auto issue_mask = [&](int st, int bufi) {
+        const uint32_t mbase = (uint32_t)(uintptr_t)(lds_void *)(m_lds + (bufi * NW + wave) * MI * 64);
+        const uint16_t *src = mrow + st * BK + 8 * half;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            const uint32_t m0 = __builtin_amdgcn_readfirstlane(mbase + i * 1024);
+            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src + 16 * i) : "memory");
+        }
+    };
+
+    const uint16_t *kbase = (const uint16_t *)a.k + b * a.k_bs + kvh * a.k_hs;
+    const uint16_t *vbase = (const uint16_t *)a.v + b * a.v_bs + kvh * a.v_hs;
+    KS kstream;
+    VS vstream;
+    kstream.init(lane, wave, a.k_rs);
+    vstream.init(lane, wave, a.v_rs);
+    int st = next_stage(0);
+    auto issue_stage = [&](int s_, int bufi) {
+        if (HAS_MASK && stage_code(s_) == TILE_MASKED && mask_in_lds(s_)) issue_mask(s_, bufi);
+        const bool full = s_ * BK + BK <= a.kv_len;
+        kstream.issue(k_lds + bufi * STAGE_ELEMS, kbase, a.k_rs, s_ * BK, a.kv_len, wave, full);
+        vstream.issue(v_lds + bufi * STAGE_ELEMS, vbase, a.v_rs, s_ * BK, a.kv_len, wave, full);
+    };
+
+    // ---- Q fragments: B operand of S^T = K Q^T, k = 16*ks + 8*half + i.  f16 K/V: scale*log2(e)
+    // folded in before rounding; bf16 Q against bf16 K/V is used as given and S is scaled after.
+    constexpr bool PRESCALE = !BF16;
+    uint4v qf[KSTEPS];
+    if (!a.q_bf16) {
+        const float *qrow = reinterpret_cast<const float *>(a.q) + b * a.q_bs + (int64_t)row_c * a.q_rs +
+                            (int64_t)head * a.q_hs + 8 * half;
+#pragma unroll
+        for (int c0 = 0; c0 < KSTEPS; c0 += 8) {
+            float4v raw[8][2];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                raw[j][0] = *reinterpret_cast<const float4v *>(qrow + 16 * (c0 + j));
+                raw[j][1] = *reinterpret_cast<const float4v *>(qrow + 16 * (c0 + j) + 4);
+            }
+            if (c0 == 0 && st < n_stages) issue_stage(st, 0);  // the first stage shares the round trip
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float4v x0 = raw[j][0] * a.score_scale, x1 = raw[j][1] * a.score_scale;
+                uint4v cv;
+                cv[0] = pack2(to_kv16<BF16>(x0[0]), to_kv16<BF16>(x0[1]));
+                cv[1] = pack2(to_kv16<BF16>(x0[2]), to_kv16<BF16>(x0[3]));
+                cv[2] = pack2(to_kv16<BF16>(x1[0]), to_kv16<BF16>(x1[1]));
+                cv[3] = pack2(to_kv16<BF16>(x1[2]), to_kv16<BF16>(x1[3]));
+                qf[c0 + j] = row_ok ? cv : uint4v{0u, 0u, 0u, 0u};
+            }
+        }
+    } else {
+        const uint16_t *qrow = reinterpret_cast<const uint16_t *>(a.q) + b * a.q_bs + (int64_t)row_c * a.q_rs +
+                               (int64_t)head * a.q_hs + 8 * half;
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) qf[ks] = *reinterpret_cast<const uint4v *>(qrow + 16 * ks);
+        if (st < n_stages) issue_stage(st, 0);
+#pragma unroll
+        for (int ks = 0; ks < KSTEPS; ++ks) {
+            if constexpr (!BF16) {
+                uint4v cv;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float lo = bf16_bits_to_f32((uint16_t)(qf[ks][e] & 0xffffu)) * a.score_scale;
+                    const float hi = bf16_bits_to_f32((uint16_t)(qf[ks][e] >> 16)) * a.score_scale;
+                    cv[e] = pack2(to_kv16<false>(lo), to_kv16<false>(hi));
+                }
+                qf[ks] = cv;
+            }
+            if (!row_ok) qf[ks] = uint4v{0u, 0u, 0u, 0u};
+        }
+    }
+    const float post_scale = PRESCALE ? 1.f : a.score_scale;
+
+    // MFMA operand reads as lane offsets plus immediates (layouts as in prefill_kernel)
+    uint32_t k_off[8];
+#pragma unroll
+    for (int r = 0; r < 8; ++r) k_off[r] = (uint32_t)((col * D + 8 * ((2 * r + half) ^ (col & 15))) * 2);
+    uint32_t v_off[4];
+    {
+        const int g16 = lane >> 4, j16 = lane & 15;
+        const int vr = 4 * (g16 >> 1) + (j16 >> 2);
+        const int l0 = 2 * (g16 & 1) + ((j16 & 3) >> 1);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v_off[q] = (uint32_t)((vr * D + 4 * (j16 & 1) + 8 * (4 * (q ^ (vr & 3)) + l0)) * 2);
+    }
+
+    float16v acc_o[DBLK];
+#pragma unroll
+    for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[db][r] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    int buf = 0;
+    while (st < n_stages) {
+        const int code = stage_code(st);
+        const int nxt = next_stage(st + 1);
+        const int key0 = st * BK;
+        const bool full_stage = key0 + BK <= a.kv_len;
+        wait_all_barrier();  // this stage's K, V and mask landed (requested one stage ago)
+        if (nxt < n_stages) issue_stage(nxt, buf ^ 1);
+        const char *kt = reinterpret_cast<const char *>(k_lds + buf * STAGE_ELEMS);
+        const char *vt = reinterpret_cast<const char *>(v_lds + buf * STAGE_ELEMS);
+
+        float16v s;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = 0.f;
+        lds_pipeline<KSTEPS, kLdsAhead, uint4v>(
+            [&](int ks) __attribute__((always_inline)) {
+                return *reinterpret_cast<const uint4v *>(kt + k_off[ks & 7] + (ks >> 3) * 256);
+            },
+            [&](int ks, const uint4v &kf) __attribute__((always_inline)) { s = mfma32<BF16>(kf, qf[ks], s); });
+
+        // scale and mask (log2 units); this lane holds keys key0 + 8*(r/4) + 4*half + r%4
+        if (HAS_MASK && code == TILE_MASKED) {
+            uint2 mr[4];
+            if (mask_in_lds(st)) {
+                const char *mb = reinterpret_cast<const char *>(m_lds + (buf * NW + wave) * MI * 64) + col * 16 + 8 * half;
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) mr[q4] = *reinterpret_cast<const uint2 *>(mb + ((q4 >> 1) * 64 + (q4 & 1) * 32) * 16);
+            } else {
+#pragma unroll
+                for (int q4 = 0; q4 < 4; ++q4) {
+                    const int kf = key0 + 8 * q4 + 4 * half;
+                    uint16_t m16[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) m16[e] = mrow[min(kf + e, a.kv_len - 1)];
+                    mr[q4] = make_uint2(pack2(m16[0], m16[1]), pack2(m16[2], m16[3]));
+                }
+            }
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t word = e < 2 ? mr[q4].x : mr[q4].y;
+                    const uint16_t m16 = (uint16_t)(word >> (16 * (e & 1)));
+                    const float mv = MBF16 ? bf16_bits_to_f32(m16) : f16_bits_to_f32(m16);
+                    s[4 * q4 + e] = PRESCALE ? fmaf(mv, kLog2e, s[4 * q4 + e]) : fmaf(s[4 * q4 + e], post_scale, mv * kLog2e);
+                }
+        } else if constexpr (!PRESCALE) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] *= post_scale;
+        }
+        if (!full_stage) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (key0 + 8 * (r >> 2) + 4 * half + (r & 3) >= a.kv_len) s[r] = -INFINITY;
+        }
+
+        // online softmax for this lane's query (16 keys here, 16 in lane ^ 32)
+        float mx = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        mx = max_with_other_half(mx);
+        const bool grow = mx > m_run + kRescaleThreshold;
+        const float m_new = grow ? mx : m_run;
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+        float rowsum = 0.f;
+        uint4v pb[2];
+        uint4v pl[BF16 ? 2 : 1];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            uint32_t w[4], wl[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float p0 = __builtin_amdgcn_exp2f(s[8 * e + 2 * i] - m_use);
+                const float p1 = __builtin_amdgcn_exp2f(s[8 * e + 2 * i + 1] - m_use);
+                if constexpr (BF16) pack_p_bf16(p0, p1, w[i], wl[i], rowsum);
+                else w[i] = pack_p_f16(p0, p1, rowsum);
+            }
+            pb[e] = uint4v{w[0], w[1], w[2], w[3]};
+            if constexpr (BF16) pl[e] = uint4v{wl[0], wl[1], wl[2], wl[3]};
+        }
+        rowsum = sum_with_other_half(rowsum);
+        l_run = l_run * alpha + rowsum;
+        m_run = m_new;
+        if (__ballot(grow)) {
+#pragma unroll
+            for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc_o[db][r] = scale_acc(acc_o[db][r], alpha);
+        }
+
+        // O^T[d][query] += V^T[d][key] P^T[key][query]; step i: P^T half u = i / DBLK into O block i % DBLK
+        lds_pipeline<2 * DBLK, kLdsAhead, uint4v>(
+            [&](int i) __attribute__((always_inline)) {
+                const int u = i / DBLK, db = i % DBLK;
+                const char *p0 = vt + v_off[db & 3] + 64 * (db & ~3) + u * 32 * D;
+                return read_tr16_pair(reinterpret_cast<const uint16_t *>(p0),
+                                      reinterpret_cast<const uint16_t *>(p0 + 16 * D));
+            },
+            [&](int i, const uint4v &vf) __attribute__((always_inline)) {
+                acc_o[i % DBLK] = mfma32<BF16>(vf, pb[i / DBLK], acc_o[i % DBLK]);
+                if constexpr (BF16) acc_o[i % DBLK] = mfma32<BF16>(vf, pl[i / DBLK], acc_o[i % DBLK]);
+            });
+        buf ^= 1;
+        st = nxt;
+    }
+
+    // ---- epilogue: O = O^T / l straight from the accumulators; lane (col, half) holds
+    // rows d = 32*db + 8*r4 + 4*half + 0..3 of its query's output row
+    if (row_ok) {
+        const float sc = l_run > 0.f ? 1.f / l_run : 0.f;
+        float *orow = a.o + b * a.o_bs + (int64_t)row * a.o_rs + (int64_t)head * a.o_hs + 4 * half;
+#pragma unroll
+        for (int db = 0; db < DBLK; ++db)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                float4v x;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = acc_o[db][4 * r4 + e] * sc;
+                *reinterpret_cast<float4v *>(orow + 32 * db + 8 * r4) = x;
+            }
+    }
+}
+
 // One wave classifies one (query block, 64-key tile): TILE_SKIP when every
 // entry is -inf, TILE_OPEN when every entry is zero, else TILE_MASKED.  The
 // pass also clears the status block and the pair counters the attention pass uses.  Only
@@ -1232,9 +1521,48 @@ int plan_prefill(const attn_prefill_params *p, PrefillPlan *plan) {
     const int D = p->head_dim;
     plan->head_dim = D;
     const bool qsplit = p->q_dtype == ATTN_F32 && p->kv_dtype == ATTN_BF16;
+    const int g = p->n_heads / p->n_kv_heads;
+    // head_dim 512 with Q in one K/V type (not the f32-Q + bf16-K/V pair): 128-slot
+    // workgroups with every wave over the whole head dim, when there are enough of them
+    // to fill the chip without splitting the KV range
+    plan->wide = 0;
+    if (D == 512 && !qsplit) {
+        int hpw = 1;  // query heads per workgroup: a power of two dividing g, at most 4 (>= 32 rows)
+        for (int d = 2; d <= 4 && d <= g; d *= 2)
+            if (g % d == 0) hpw = d;
+        const int rpw = 128 / hpw;
+        const int64_t wgs = (int64_t)p->batch * ((p->rows + rpw - 1) / rpw) * (p->n_heads / hpw);
+        if (wgs >= 256) {
+            plan->wide = 1;
+            plan->slices = 1;
+            plan->slice_dim = D;
+            plan->rows_per_wg = rpw;
+            plan->heads_per_wg = hpw;
+            plan->query_waves = 4;
+            plan->waves = 4;
+            plan->row_blocks = (p->rows + rpw - 1) / rpw;
+            plan->head_groups = p->n_heads / hpw;
+            plan->kv_tiles = (p->kv_len + kTile - 1) / kTile;
+            plan->blk_stride = (plan->kv_tiles + 3) & ~3;
+            plan->splits = 1;
+            plan->tiles_per_split = plan->kv_tiles;
+            plan->pairing = 0;
+            plan->status_offset = 0;
+            size_t off = ATTN_PREFILL_STATUS_BYTES;
+            const int blk_heads = p->m_hs == 0 ? 1 : plan->head_groups;
+            plan->blk_bytes = p->mask_dtype != ATTN_NONE
+                                  ? (size_t)p->batch * blk_heads * plan->row_blocks * plan->blk_stride : 0;
+            plan->blk_offset = off;
+            off = align256(off + plan->blk_bytes);
+            plan->ml_offset = plan->ml_bytes = plan->part_offset = plan->part_bytes = 0;
+            plan->pair_cnt_offset = plan->pair_cnt_bytes = plan->pair_ml_offset = plan->pair_ml_bytes = 0;
+            plan->pair_part_offset = plan->pair_part_bytes = 0;
+            plan->workspace_bytes = off;
+            return ATTN_OK;
+        }
+    }
     plan->slices = D > 256 ? 2 : 1;
     plan->slice_dim = D / plan->slices;
-    const int g = p->n_heads / p->n_kv_heads;
     // 4 waves hold 128 query slots (64 with two head-dim slices); at least 64 slots.
     // f32 Q against bf16 K/V at head_dim 256 (Q carried as a hi + lo pair) runs two-wave
     // workgroups of 64 slots: the four-wave build does not fit the register file.
@@ -1370,6 +1698,20 @@ hipError_t launch_prefill(const attn_prefill_params *p, const PrefillPlan *plan,
         if (err != hipSuccess) return err;
     }
     const bool bf16 = p->kv_dtype == ATTN_BF16;
+    if (plan->wide) {
+        const dim3 grid((unsigned)((int64_t)plan->head_groups * plan->row_blocks * p->batch));
+        const int mask = a.mask == nullptr ? 0 : a.mask_bf16 ? 2 : 1;
+        if (bf16) {
+            if (mask == 0) hipLaunchKernelGGL((wide_kernel<512, true, 0>), grid, dim3(256), 0, stream, a);
+            else if (mask == 1) hipLaunchKernelGGL((wide_kernel<512, true, 1>), grid, dim3(256), 0, stream, a);
+            else hipLaunchKernelGGL((wide_kernel<512, true, 2>), grid, dim3(256), 0, stream, a);
+        } else {
+            if (mask == 0) hipLaunchKernelGGL((wide_kernel<512, false, 0>), grid, dim3(256), 0, stream, a);
+            else if (mask == 1) hipLaunchKernelGGL((wide_kernel<512, false, 1>), grid, dim3(256), 0, stream, a);
+            else hipLaunchKernelGGL((wide_kernel<512, false, 2>), grid, dim3(256), 0, stream, a);
+        }
+        return hipGetLastError();
+    }
     switch (plan->head_dim) {
     case 128: return launch_for_dim<128>(a, plan, bf16, stream);
     case 256: return launch_for_dim<256>(a, plan, bf16, stream);
