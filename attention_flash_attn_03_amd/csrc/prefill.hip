@@ -38,6 +38,7 @@
 #include <math.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "device_common.h"
 #include "internal.h"
@@ -149,6 +150,16 @@ constexpr int kAgentCoherent = 16;
 
 constexpr int cgcd(int x, int y) { return y == 0 ? x : cgcd(y, x % y); }
 
+// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // A wave-uniform pointer, made visibly uniform so that it can live in SGPRs.
 __device__ __forceinline__ const char *uniform_ptr(const char *p) {
     const uint64_t v = (uint64_t)(uintptr_t)p;
@@ -230,6 +241,22 @@ struct TileStream {
                                           int kv_len, int wave, bool full) const {
         if (full && row_stride < kOff32Stride) issue_full(lds, base, row_stride, key0, wave);
         else issue_tail(lds, base, row_stride, key0, kv_len, wave);
+    }
+    // A full stage one instruction at a time, so that its loads can be spread between
+    // other work: stage_ptr once per stage, then issue_one for it = 0 .. NLD-1 (it a
+    // compile-time constant).
+    __device__ __forceinline__ static const char *stage_ptr(const uint16_t *base, int64_t row_stride, int key0,
+                                                            int wave) {
+        return uniform_ptr((const char *)(base + (int64_t)(key0 + wave * RPI) * row_stride));
+    }
+    __device__ __forceinline__ void issue_one(uint16_t *lds, const char *stage, int64_t row_stride, int it,
+                                              int wave) const {
+        const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void *)lds;
+        const uint32_t step = (uint32_t)(GR * row_stride * 2);
+        const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base + (it * NW + wave) * 1024);
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff[it % P] + it * step),
+                     "s"(stage)
+                     : "memory");
     }
 };
 
@@ -1202,7 +1229,36 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int key0 = st * BK;
         const bool full_stage = key0 + BK <= a.kv_len;
         wait_all_barrier();  // this stage's K, V and mask landed (requested one stage ago)
-        if (nxt < n_stages) issue_stage(nxt, buf ^ 1);
+        // The next stage's loads.  Issued together they stall the wave until the memory
+        // pipeline has taken them (72 KB per stage per CU); a full stage is therefore
+        // issued one instruction at a time between the S MFMAs below.  A ragged or widely
+        // strided stage is issued at once here.
+        const bool nfull = nxt < n_stages && nxt * BK + BK <= a.kv_len && a.k_rs < kOff32Stride &&
+                           a.v_rs < kOff32Stride;
+        if (nxt < n_stages && !nfull) issue_stage(nxt, buf ^ 1);
+        const bool nmask = HAS_MASK && nfull && stage_code(nxt) == TILE_MASKED && mask_in_lds(nxt);
+        const char *kst = KS::stage_ptr(kbase, a.k_rs, nxt * BK, wave);
+        const char *vst = VS::stage_ptr(vbase, a.v_rs, nxt * BK, wave);
+        uint16_t *kdst = k_lds + (buf ^ 1) * STAGE_ELEMS;
+        uint16_t *vdst = v_lds + (buf ^ 1) * STAGE_ELEMS;
+        const uint32_t mdst = (uint32_t)(uintptr_t)(lds_void *)(m_lds + ((buf ^ 1) * NW + wave) * MI * 64);
+        // instruction n of the next stage: mask chunks first, then K and V alternately
+        constexpr int NDMA = (HAS_MASK ? MI : 0) + 2 * KS::NLD;
+        auto dma_one = [&](auto n_c) __attribute__((always_inline)) {
+            constexpr int n = decltype(n_c)::value;
+            if constexpr (HAS_MASK && n < MI) {
+                if (nmask) {
+                    const uint32_t m0 = __builtin_amdgcn_readfirstlane(mdst + n * 1024);
+                    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0),
+                                 "v"(mrow + nxt * BK + 8 * half + 16 * n)
+                                 : "memory");
+                }
+            } else {
+                constexpr int j = n - (HAS_MASK ? MI : 0);
+                if constexpr (j % 2 == 0) kstream.issue_one(kdst, kst, a.k_rs, j / 2, wave);
+                else vstream.issue_one(vdst, vst, a.v_rs, j / 2, wave);
+            }
+        };
         const char *kt = reinterpret_cast<const char *>(k_lds + buf * STAGE_ELEMS);
         const char *vt = reinterpret_cast<const char *>(v_lds + buf * STAGE_ELEMS);
 
@@ -1213,7 +1269,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             [&](int ks) __attribute__((always_inline)) {
                 return *reinterpret_cast<const uint4v *>(kt + k_off[ks & 7] + (ks >> 3) * 256);
             },
-            [&](int ks, const uint4v &kf) __attribute__((always_inline)) { s = mfma32<BF16>(kf, qf[ks], s); });
+            [&](int ks, const uint4v &kf) __attribute__((always_inline)) {
+                s = mfma32<BF16>(kf, qf[ks], s);
+                if (nfull) {
+                    // instruction n at step n * KSTEPS / NDMA
+                    static_for<NDMA>([&](auto n_c) __attribute__((always_inline)) {
+                        if (ks == (decltype(n_c)::value * KSTEPS) / NDMA) dma_one(n_c);
+                    });
+                }
+            });
 
         // scale and mask (log2 units); this lane holds keys key0 + 8*(r/4) + 4*half + r%4
         if (HAS_MASK && code == TILE_MASKED) {
