@@ -765,13 +765,41 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
 
         wait_all_barrier();  // K, V and mask of this stage landed (all requested one stage ago)
 
-        // request stage nxt into the other buffers
-        if (nxt < st_end) {
+        // Request stage nxt into the other buffers.  Issued together the loads stall the wave
+        // until the memory pipeline has taken them; a full stage is therefore issued one
+        // instruction at a time between the S MFMAs below (a ragged or widely strided stage
+        // at once, here).
+        const bool nfull = nxt < st_end && nxt * BK + BK <= a.kv_len && a.k_rs < kOff32Stride &&
+                           a.v_rs < kOff32Stride;
+        if (nxt < st_end && !nfull) {
             if (HAS_MASK && slice == 0 && stage_code(nxt) == TILE_MASKED && mask_in_lds(nxt)) issue_mask(nxt, buf ^ 1);
-            const bool nfull = nxt * BK + BK <= a.kv_len;
-            kstream.issue(k_lds + (buf ^ 1) * STAGE_ELEMS, kbase, a.k_rs, nxt * BK, a.kv_len, wave, nfull);
-            vstream.issue(v_lds + (buf ^ 1) * STAGE_ELEMS, vbase, a.v_rs, nxt * BK, a.kv_len, wave, nfull);
+            kstream.issue(k_lds + (buf ^ 1) * STAGE_ELEMS, kbase, a.k_rs, nxt * BK, a.kv_len, wave, false);
+            vstream.issue(v_lds + (buf ^ 1) * STAGE_ELEMS, vbase, a.v_rs, nxt * BK, a.kv_len, wave, false);
         }
+        const bool nmask = HAS_MASK && nfull && slice == 0 && stage_code(nxt) == TILE_MASKED && mask_in_lds(nxt);
+        const char *kst = KS::stage_ptr(kbase, a.k_rs, nxt * BK, wave);
+        const char *vst = VS::stage_ptr(vbase, a.v_rs, nxt * BK, wave);
+        uint16_t *kdst = k_lds + (buf ^ 1) * STAGE_ELEMS;
+        uint16_t *vdst = v_lds + (buf ^ 1) * STAGE_ELEMS;
+        const uint32_t mdst = (uint32_t)(uintptr_t)(lds_void *)(m_lds + ((buf ^ 1) * QW + qwave) * MI * 64);
+        // instruction n of the next stage: mask chunks first, then K and V alternately
+        constexpr int NDMA = (HAS_MASK ? MI : 0) + 2 * KS::NLD;
+        static_assert(KS::NLD == VS::NLD, "K and V stream alike");
+        auto dma_one = [&](auto n_c) __attribute__((always_inline)) {
+            constexpr int n = decltype(n_c)::value;
+            if constexpr (HAS_MASK && n < MI) {
+                if (nmask) {
+                    const uint32_t m0 = __builtin_amdgcn_readfirstlane(mdst + n * 1024);
+                    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0),
+                                 "v"(mrow + nxt * BK + 8 * half + 16 * n)
+                                 : "memory");
+                }
+            } else {
+                constexpr int j = n - (HAS_MASK ? MI : 0);
+                if constexpr (j % 2 == 0) kstream.issue_one(kdst, kst, a.k_rs, j / 2, wave);
+                else vstream.issue_one(vdst, vst, a.v_rs, j / 2, wave);
+            }
+        };
         const uint16_t *kt_lds = k_lds + buf * STAGE_ELEMS;
         const uint16_t *vt_lds = v_lds + buf * STAGE_ELEMS;
 
@@ -791,6 +819,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
             [&](int i, const uint4v &kf) __attribute__((always_inline)) {
                 s[i % NB] = mfma32<BF16>(kf, qf[i / NB], s[i % NB]);
                 if constexpr (QSPLIT) s[i % NB] = mfma32<BF16>(kf, qlo[i / NB], s[i % NB]);
+                if (nfull) {
+                    // instruction n at step n * (S steps) / NDMA
+                    static_for<NDMA>([&](auto n_c) __attribute__((always_inline)) {
+                        if (i == (decltype(n_c)::value * NB * KSTEPS) / NDMA) dma_one(n_c);
+                    });
+                }
             });
 
         // ---- scale and mask (log2 units); this lane holds keys key0 + 32*bb + 8*(r/4) + 4*half + r%4
