@@ -70,7 +70,7 @@ TRAFFIC_ROWS = {
                "sources": ["attention_flash_attn_03_amd/csrc/decode.hip",
                            "attention_flash_attn_03_amd/csrc/device_common.h"]},
     "prefill": {"file": "prefill_chunked8k_traffic.json",
-                "kernels": {"classify": "classify_kernel", "attention": "prefill_kernel"},
+                "kernels": {"classify": "classify_kernel", "attention": "wide_kernel"},
                 "sources": ["attention_flash_attn_03_amd/csrc/prefill.hip",
                             "attention_flash_attn_03_amd/csrc/device_common.h",
                             "attention_flash_attn_03_amd/csrc/internal.h"]},

@@ -56,3 +56,18 @@ def test_traffic_is_withheld_once_a_source_changes(tmp_path, monkeypatch):
     with open(tmp_path / rec["sources"][0], "a") as f:
         f.write("\n// edited\n")
     assert bench.measured_traffic() is None
+
+
+def test_prefill_traffic_records_are_consistent():
+    """Each prefill traffic record names its kernels' sources; while they are unchanged
+    bench.py reports the recorded bytes, which exceed the algorithmic ones."""
+    for row in ("prefill", "causal2k"):
+        spec = bench.TRAFFIC_ROWS[row]
+        with open(os.path.join(ROOT, "profiles", spec["file"])) as f:
+            rec = json.load(f)
+        assert rec["sources"] == spec["sources"]
+        assert set(rec["fetch_kib"]) == set(spec["kernels"])
+        got = bench.measured_traffic(row)
+        if got is not None:
+            assert got == rec["bytes_per_launch"]
+            assert got > rec["algorithmic_bytes"]
