@@ -260,6 +260,29 @@ struct TileStream {
     }
 };
 
+// S^T accumulation kept in VGPRs.  A kernel that holds O in AGPRs gets AGPR accumulators
+// for every MFMA the compiler emits, so an S accumulator there would evict an O block to
+// VGPRs and back on every stage.  Written out, the chain's accumulator stays in VGPRs
+// (dst = srcC, which back-to-back MFMAs of one opcode accumulate without wait states).  The
+// compiler cannot see these MFMAs for its hazard checks: s_wait_after_mfma_vgpr() must
+// separate the last of them from any other read of the accumulator.
+__device__ __forceinline__ void mfma_f16_vacc_first(float16v &d, const uint4v &a, const uint4v &b) {
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_f16_vacc(float16v &d, const uint4v &a, const uint4v &b) {
+    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_bf16_vacc_first(float16v &d, const uint4v &a, const uint4v &b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_bf16_vacc(float16v &d, const uint4v &a, const uint4v &b) {
+    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
+}
+// 16 wait states: more than an 8-pass XDL result needs before a VALU, LDS or memory read of it.
+__device__ __forceinline__ void s_wait_after_mfma_vgpr(float16v &d) {
+    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(d));
+}
+
 // x *= f for an accumulator element that lives in an AGPR.  Written out so that
 // the only vector-ALU access to the O accumulator is this rare rescale: the
 // compiler then keeps the accumulator in AGPRs next to the MFMAs instead of
@@ -1297,14 +1320,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const char *vt = reinterpret_cast<const char *>(v_lds + buf * STAGE_ELEMS);
 
         float16v s;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = 0.f;
         lds_pipeline<KSTEPS, kLdsAhead, uint4v>(
             [&](int ks) __attribute__((always_inline)) {
                 return *reinterpret_cast<const uint4v *>(kt + k_off[ks & 7] + (ks >> 3) * 256);
             },
             [&](int ks, const uint4v &kf) __attribute__((always_inline)) {
-                s = mfma32<BF16>(kf, qf[ks], s);
+                if constexpr (BF16) {
+                    if (ks == 0) mfma_bf16_vacc_first(s, kf, qf[ks]);
+                    else mfma_bf16_vacc(s, kf, qf[ks]);
+                } else {
+                    if (ks == 0) mfma_f16_vacc_first(s, kf, qf[ks]);
+                    else mfma_f16_vacc(s, kf, qf[ks]);
+                }
                 if (nfull) {
                     // instruction n at step n * KSTEPS / NDMA
                     static_for<NDMA>([&](auto n_c) __attribute__((always_inline)) {
@@ -1312,6 +1339,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     });
                 }
             });
+
+        s_wait_after_mfma_vgpr(s);
 
         // scale and mask (log2 units); this lane holds keys key0 + 8*(r/4) + 4*half + r%4
         if (HAS_MASK && code == TILE_MASKED) {
