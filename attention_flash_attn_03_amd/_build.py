@@ -31,6 +31,11 @@ CFLAGS = [
 ]
 
 
+# per-file additions: the narrow prefill kernel keeps its MFMA accumulators in
+# ordinary VGPRs, so its 256 registers per wave form one pool
+EXTRA_FLAGS = {"narrow.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def source_files() -> list:
     """Every file libattn.so is compiled from: the HIP sources, their headers and the C ABI header."""
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.h"))) + [HEADER]
@@ -48,7 +53,8 @@ def source_digest() -> str:
 
 def _compile(src: str, digest: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, '-DATTN_SOURCE_SHA256="%s"' % digest, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), '-DATTN_SOURCE_SHA256="%s"' % digest,
+           "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if "packed-fp32-ops" not in l)
     if res.returncode != 0:

@@ -26,6 +26,7 @@ struct PrefillPlan {
     int blk_stride;                   // bytes per row of tile codes (kv_tiles rounded up to 4)
     int splits, tiles_per_split;      // KV range split across workgroups
     int wide;                         // head_dim 512 in 128-slot workgroups, each wave over the whole head dim
+    int narrow;                       // head_dim <= 256 in 128-slot workgroups of eight 16-slot waves
     size_t status_offset;             // status block (ATTN_PREFILL_STATUS_BYTES) at the workspace start
     size_t blk_bytes, blk_offset;     // tile codes [batch][blk heads][row_blocks][blk_stride]
     size_t part_offset, part_bytes;   // split partials: O [splits][batch][n_heads][rows][D] f32

@@ -35,274 +35,10 @@
 //    (agent-coherent buffer accesses and a relaxed atomic counter, no fence).
 //    Calls with few query blocks split the KV range across workgroups with a
 //    log-sum-exp combine pass.
-#include <math.h>
-
-#include <type_traits>
-#include <utility>
-
-#include "device_common.h"
-#include "internal.h"
+#include "prefill_common.h"
 
 namespace attn {
 namespace {
-
-constexpr int kTile = 64;               // KV rows per step
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kLdsAhead = 4;            // MFMA operand reads in flight ahead of their MFMA
-
-// O and l are rescaled only when a row's running max grows by more than this
-// many binary orders of magnitude; until then the stale max stays the
-// reference, so P <= 2^8 (fine in f16, bf16 and the fp32 sums) and O / l is
-// unchanged.  Rescales then happen a few times per row instead of per tile.
-constexpr float kRescaleThreshold = 8.f;
-
-// Words of the status block at the start of the workspace (ATTN_PREFILL_STATUS_BYTES).
-constexpr int kStatusWords = ATTN_PREFILL_STATUS_BYTES / 4;
-// Polls of a partner's ready flag before the wait gives up (each poll sleeps ~128 clocks).
-constexpr int kPairWaitPolls = 1 << 22;
-
-struct PrefillArgs {
-    const void *q, *k, *v, *mask;
-    float *o;
-    const uint8_t *blk;
-    float *part;       // split partials (unnormalised O)
-    float2 *ml;        // split partials (running max in log2 units, running sum)
-    float *pair_part;  // paired row blocks: unnormalised O of each side [pairs][2][slots][D]
-    float2 *pair_ml;   // paired row blocks: (m, l) of each side [pairs][2][slots]
-    uint32_t *pair_cnt;  // paired row blocks: [pairs][arrivals, partial ready] (zeroed by the classify pass)
-    uint32_t *status;    // status block: [0] error flags, [1] merged row blocks (zeroed at the start of every call)
-    int64_t q_bs, q_rs, q_hs, k_bs, k_rs, k_hs, v_bs, v_rs, v_hs, m_bs, m_hs, m_rs, o_bs, o_rs, o_hs;
-    int batch, rows, kv_len, n_heads, group;
-    int rows_per_wg, heads_per_wg, row_blocks, head_groups, blk_heads;
-    int kv_tiles, blk_stride, splits, tiles_per_split;
-    int q_bf16, mask_bf16, mask_vec, mask_dma, pairing, n_pair_cnt;
-    float score_scale;  // scale * log2(e)
-};
-
-typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-typedef __bf16 bhalf2v __attribute__((ext_vector_type(2)));
-
-template <bool BF16>
-__device__ __forceinline__ float16v mfma32(uint4v a, uint4v b, float16v c) {
-    if constexpr (BF16) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bhalf8, a), __builtin_bit_cast(bhalf8, b),
-                                                       c, 0, 0, 0);
-    } else {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(half8, a), __builtin_bit_cast(half8, b), c,
-                                                      0, 0, 0);
-    }
-}
-
-template <bool BF16>
-__device__ __forceinline__ uint16_t to_kv16(float x) {
-    if constexpr (BF16) {
-        return f32_to_bf16_rne(x);
-    } else {
-        return __builtin_bit_cast(uint16_t, (_Float16)x);
-    }
-}
-
-// Two probabilities rounded to f16 (v_cvt_pk_f16_f32) and their exact sum as
-// rounded (v_dot2 against (1, 1), fp32 accumulation), so that the rounding
-// cancels in O / l.
-__device__ __forceinline__ uint32_t pack_p_f16(float p0, float p1, float &sum) {
-    const half2v v = {(_Float16)p0, (_Float16)p1};
-    sum = __builtin_amdgcn_fdot2(v, half2v{(_Float16)1.f, (_Float16)1.f}, sum, false);
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-// Two probabilities as bf16 hi + lo pairs (about 16 significant bits; one bf16
-// rounding, 2^-9 relative, breaks the error bound for a row that sees only a
-// few keys), and their f32 sum.
-__device__ __forceinline__ void pack_p_bf16(float p0, float p1, uint32_t &hi, uint32_t &lo, float &sum) {
-    const bhalf2v h = {(__bf16)p0, (__bf16)p1};
-    const bhalf2v l = {(__bf16)(p0 - (float)h[0]), (__bf16)(p1 - (float)h[1])};
-    sum += p0 + p1;
-    hi = __builtin_bit_cast(uint32_t, h);
-    lo = __builtin_bit_cast(uint32_t, l);
-}
-
-typedef __attribute__((address_space(3))) short4v lds_short4;
-typedef __attribute__((address_space(3))) void lds_void;
-typedef const __attribute__((address_space(4))) uint32_t const_u32;
-
-// two consecutive ds_read_b64_tr_b16 results form one MFMA operand as read
-__device__ __forceinline__ uint4v read_tr16_pair(const uint16_t *p0, const uint16_t *p1) {
-    const uint2 lo = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)p0));
-    const uint2 hi = __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_short4 *)p1));
-    return uint4v{lo.x, lo.y, hi.x, hi.y};
-}
-
-// LDS tile layouts (64 rows x D, no padding).  Chunk = 16 bytes = 8 elements.
-//  K: logical chunk c of row r sits at physical chunk c ^ (r % 16); the S^T
-//     A-operand read (16 consecutive rows, one chunk) hits 16 distinct banks.
-//  V: logical chunk c of row r sits at physical chunk c ^ 4*(r % 4); the
-//     transposing read (4 consecutive rows x 4 chunks per 32 lanes) hits 16
-//     distinct bank groups.
-
-// Row strides (elements) below this keep every offset inside a 64-row stage under 2^32 bytes.
-constexpr int64_t kOff32Stride = (int64_t)1 << 25;
-
-// Raw buffer descriptors (word 3 of the resource) and the cache policy that makes a
-// buffer access coherent at agent scope (sc1).
-constexpr int kRawBufferFlags = 0x00020000;
-constexpr int kAgentCoherent = 16;
-
-constexpr int cgcd(int x, int y) { return y == 0 ? x : cgcd(y, x % y); }
-
-// f(std::integral_constant<int, i>) for i = 0 .. N-1, unrolled at compile time.
-template <typename F, int... I>
-__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, I...>) {
-    (f(std::integral_constant<int, I>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F &&f) {
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// A wave-uniform pointer, made visibly uniform so that it can live in SGPRs.
-__device__ __forceinline__ const char *uniform_ptr(const char *p) {
-    const uint64_t v = (uint64_t)(uintptr_t)p;
-    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-    return (const char *)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
-
-// Streams BK-row stages of K or V into LDS with global_load_lds_dwordx4: a
-// wave-instruction fills 64 consecutive 16-byte LDS slots starting at M0, so
-// each lane fetches the global chunk that belongs in its slot.  Instruction
-// `it` of wave w covers rows row0 = (it*NW + w)*RPI .. +RPI-1; a lane's row
-// within them (lrow) is fixed and its swizzled chunk repeats with a short
-// period in `it`, so the lane offsets are computed once and each instruction
-// only needs a scalar row base (no vector arithmetic per load).  Rows past
-// kv_len (last stage only) fetch row kv_len-1: finite data whose keys are
-// masked to -inf.
-//
-// The loads are issued from inline asm so the compiler does not treat every
-// later LDS read as dependent on them (its conservative vmcnt(0) would drain
-// the prefetch of the next stage); the explicit waits in the kernel cover
-// them.  M0 is a reserved register that inline asm may not declare
-// clobbered; nothing else in these kernels reads it (no movrel, sendmsg or
-// LDS-DMA intrinsic), so writing it here is safe.
-template <int D, int NW, int BK, bool IS_V>
-struct TileStream {
-    static constexpr int CH = D / 8;
-    static constexpr int RPI = 64 / CH;                  // rows per instruction
-    static constexpr int GR = NW * RPI;                  // rows one instruction of every wave covers
-    static constexpr int NLD = BK / GR;                  // instructions per wave per stage
-    // the swizzle term of instruction `it` repeats with period P in `it`
-    static constexpr int PERIOD_ROWS = IS_V ? 4 : 16;
-    static constexpr int P = PERIOD_ROWS / cgcd(PERIOD_ROWS, GR) < NLD ? PERIOD_ROWS / cgcd(PERIOD_ROWS, GR) : NLD;
-    int lrow, inv;
-    uint32_t voff[P];   // byte offset of this lane's 16 bytes from the instruction's first row
-
-    __device__ __forceinline__ void init(int lane, int wave, int64_t row_stride) {
-        lrow = lane / CH;
-        const int lch = lane % CH;
-        inv = lch ^ (IS_V ? 4 * lrow : lrow);
-#pragma unroll
-        for (int r = 0; r < P; ++r)
-            voff[r] = (uint32_t)((lrow * row_stride + 8 * (inv ^ uniform_swz((r * NW + wave) * RPI))) * 2);
-    }
-    __device__ __forceinline__ static int uniform_swz(int row0) { return IS_V ? 4 * (row0 & 3) : (row0 & 15); }
-
-    // A stage of BK rows that all exist: one scalar base per stage and a 32-bit
-    // lane offset per instruction (the row stride times BK rows fits in 32 bits,
-    // which the caller checks).
-    __device__ __forceinline__ void issue_full(uint16_t *lds, const uint16_t *base, int64_t row_stride, int key0,
-                                               int wave) const {
-        const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void *)lds;
-        const char *stage = uniform_ptr((const char *)(base + (int64_t)(key0 + wave * RPI) * row_stride));
-        const uint32_t step = (uint32_t)(GR * row_stride * 2);
-#pragma unroll
-        for (int it = 0; it < NLD; ++it) {
-            const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base + (it * NW + wave) * 1024);
-            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff[it % P] + it * step),
-                         "s"(stage)
-                         : "memory");
-        }
-    }
-    // The ragged last stage: rows past kv_len fetch row kv_len-1 instead.
-    __device__ __forceinline__ void issue_tail(uint16_t *lds, const uint16_t *base, int64_t row_stride, int key0,
-                                               int kv_len, int wave) const {
-        const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void *)lds;
-#pragma unroll 1
-        for (int it = 0; it < NLD; ++it) {
-            const int row0 = (it * NW + wave) * RPI;
-            const int ch = inv ^ uniform_swz(row0);
-            int grow = key0 + row0 + lrow;
-            grow = grow < kv_len ? grow : kv_len - 1;
-            const uint16_t *src = base + (int64_t)grow * row_stride + ch * 8;
-            const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base + (it * NW + wave) * 1024);
-            asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(m0), "v"(src) : "memory");
-        }
-    }
-    __device__ __forceinline__ void issue(uint16_t *lds, const uint16_t *base, int64_t row_stride, int key0,
-                                          int kv_len, int wave, bool full) const {
-        if (full && row_stride < kOff32Stride) issue_full(lds, base, row_stride, key0, wave);
-        else issue_tail(lds, base, row_stride, key0, kv_len, wave);
-    }
-    // A full stage one instruction at a time, so that its loads can be spread between
-    // other work: stage_ptr once per stage, then issue_one for it = 0 .. NLD-1 (it a
-    // compile-time constant).
-    __device__ __forceinline__ static const char *stage_ptr(const uint16_t *base, int64_t row_stride, int key0,
-                                                            int wave) {
-        return uniform_ptr((const char *)(base + (int64_t)(key0 + wave * RPI) * row_stride));
-    }
-    __device__ __forceinline__ void issue_one(uint16_t *lds, const char *stage, int64_t row_stride, int it,
-                                              int wave) const {
-        const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void *)lds;
-        const uint32_t step = (uint32_t)(GR * row_stride * 2);
-        const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_base + (it * NW + wave) * 1024);
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" ::"s"(m0), "v"(voff[it % P] + it * step),
-                     "s"(stage)
-                     : "memory");
-    }
-};
-
-// S^T accumulation kept in VGPRs.  A kernel that holds O in AGPRs gets AGPR accumulators
-// for every MFMA the compiler emits, so an S accumulator there would evict an O block to
-// VGPRs and back on every stage.  Written out, the chain's accumulator stays in VGPRs
-// (dst = srcC, which back-to-back MFMAs of one opcode accumulate without wait states).  The
-// compiler cannot see these MFMAs for its hazard checks: s_wait_after_mfma_vgpr() must
-// separate the last of them from any other read of the accumulator.
-__device__ __forceinline__ void mfma_f16_vacc_first(float16v &d, const uint4v &a, const uint4v &b) {
-    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_f16_vacc(float16v &d, const uint4v &a, const uint4v &b) {
-    asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_bf16_vacc_first(float16v &d, const uint4v &a, const uint4v &b) {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(d) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void mfma_bf16_vacc(float16v &d, const uint4v &a, const uint4v &b) {
-    asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(d) : "v"(a), "v"(b));
-}
-// 16 wait states: more than an 8-pass XDL result needs before a VALU, LDS or memory read of it.
-__device__ __forceinline__ void s_wait_after_mfma_vgpr(float16v &d) {
-    asm volatile("s_nop 7\n\ts_nop 7" : "+v"(d));
-}
-
-// x *= f for an accumulator element that lives in an AGPR.  Written out so that
-// the only vector-ALU access to the O accumulator is this rare rescale: the
-// compiler then keeps the accumulator in AGPRs next to the MFMAs instead of
-// copying it to VGPRs on every stage.
-__device__ __forceinline__ float scale_acc(float x, float f) {
-    float t;
-    asm volatile("v_accvgpr_read_b32 %1, %0\n\tv_mul_f32 %1, %1, %2\n\tv_accvgpr_write_b32 %0, %1"
-                 : "+a"(x), "=&v"(t)
-                 : "v"(f));
-    return x;
-}
-
-// Wait until every vector-memory operation and every LDS read of this wave has
-// completed, then meet the other waves.  At the start of a stage this is the one
-// barrier of the stage: once every wave is past it, no wave reads the previous
-// stage's buffers any more, so the next stage may be requested into them.
-__device__ __forceinline__ void wait_all_barrier() {
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-__device__ __forceinline__ void lds_done_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // QSPLIT: f32 Q against bf16 K/V.  bf16 keeps 8 significant bits, which
 // perturbs every score by about 2^-9 relative; Q is carried as hi + lo bf16
@@ -338,8 +74,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
     constexpr int NB = BK / 32;                // 32-key blocks per stage
     constexpr int SPT = kTile / BK;            // stages per 64-key tile code
     constexpr int STAGE_ELEMS = BK * D;
-    using KS = TileStream<D, NW, BK, false>;
-    using VS = TileStream<D, NW, BK, true>;
+    using KS = TileStream<D, NW, BK, kSwzK>;
+    using VS = TileStream<D, NW, BK, kSwzV32>;
     __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2 * STAGE_ELEMS];
     __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2 * STAGE_ELEMS];
     __shared__ __attribute__((aligned(16))) float4v x_lds[NS > 1 ? NW * NB * 4 * 64 : 1];
@@ -1136,8 +872,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     constexpr int SPT = kTile / BK;
     constexpr int STAGE_ELEMS = BK * D;
     constexpr int MI = 2 * NB;                 // mask DMA instructions per wave per stage
-    using KS = TileStream<D, NW, BK, false>;
-    using VS = TileStream<D, NW, BK, true>;
+    using KS = TileStream<D, NW, BK, kSwzK>;
+    using VS = TileStream<D, NW, BK, kSwzV32>;
     __shared__ __attribute__((aligned(1024))) uint16_t k_lds[2 * STAGE_ELEMS];
     __shared__ __attribute__((aligned(1024))) uint16_t v_lds[2 * STAGE_ELEMS];
     __shared__ __attribute__((aligned(1024))) uint4v m_lds[HAS_MASK ? 2 * NW * MI * 64 : 1];
@@ -1653,6 +1389,7 @@ int plan_prefill(const attn_prefill_params *p, PrefillPlan *plan) {
     // workgroups with every wave over the whole head dim, when there are enough of them
     // to fill the chip without splitting the KV range
     plan->wide = 0;
+    plan->narrow = 0;
     if (D == 512 && !qsplit) {
         int hpw = 1;  // query heads per workgroup: a power of two dividing g, at most 4 (>= 32 rows)
         for (int d = 2; d <= 4 && d <= g; d *= 2)
@@ -1690,10 +1427,10 @@ int plan_prefill(const attn_prefill_params *p, PrefillPlan *plan) {
     }
     plan->slices = D > 256 ? 2 : 1;
     plan->slice_dim = D / plan->slices;
-    // 4 waves hold 128 query slots (64 with two head-dim slices); at least 64 slots.
-    // f32 Q against bf16 K/V at head_dim 256 (Q carried as a hi + lo pair) runs two-wave
-    // workgroups of 64 slots: the four-wave build does not fit the register file.
-    const int max_slots = (plan->slices == 1 && !(qsplit && D == 256)) ? 128 : 64;
+    // 128 query slots per workgroup (64 with two head-dim slices); at least 64 slots.
+    // 128-slot workgroups at head_dim <= 256 run the eight-wave narrow kernel; 64-slot
+    // ones the two-wave prefill_kernel.
+    const int max_slots = plan->slices == 1 ? 128 : 64;
     int rpw = pow2_at_least(p->rows < 32 ? p->rows : 32);
     int hpw = 1;  // a power of two, so rows_per_wg * heads_per_wg can reach a multiple of 32
     for (int d = 1; d <= g; d *= 2)
@@ -1710,6 +1447,7 @@ int plan_prefill(const attn_prefill_params *p, PrefillPlan *plan) {
     }
     plan->rows_per_wg = rpw;
     plan->heads_per_wg = hpw;
+    plan->narrow = plan->slices == 1 && rpw * hpw == 128;
     plan->query_waves = rpw * hpw / 32;
     plan->waves = plan->query_waves * plan->slices;
     if (plan->waves != 4 && !(plan->waves == 2 && plan->slices == 1)) return ATTN_EINVAL;
@@ -1838,6 +1576,12 @@ hipError_t launch_prefill(const attn_prefill_params *p, const PrefillPlan *plan,
             else hipLaunchKernelGGL((wide_kernel<512, false, 2>), grid, dim3(256), 0, stream, a);
         }
         return hipGetLastError();
+    }
+    if (plan->narrow) {
+        hipError_t err = launch_narrow_prefill(a, plan, bf16, stream);
+        if (err != hipSuccess) return err;
+        if (plan->splits > 1) return plan->head_dim == 128 ? launch_combine<128>(a, stream) : launch_combine<256>(a, stream);
+        return hipSuccess;
     }
     switch (plan->head_dim) {
     case 128: return launch_for_dim<128>(a, plan, bf16, stream);

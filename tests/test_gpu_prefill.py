@@ -84,7 +84,7 @@ def test_prefill_oracle_sized(orc, rows, kv_len, cached, h, hk, d, holes, seed):
     (512, 32, 16, 128, 2, "f16"),  # 256 workgroups, every pair shared
     (512, 16, 8, 512, 2, "f16"),   # head_dim 512 (two head-dim slices), 256 workgroups
     (192, 2, 1, 128, 1, "bf16"),   # f32 Q + bf16 K/V; the first rows see one to a few keys
-    (1024, 16, 8, 256, 1, "bf16"),  # two-wave workgroups: 256 of them
+    (1024, 16, 8, 256, 2, "bf16"),  # eight-wave workgroups: 256 of them
     (512, 16, 8, 512, 2, "bf16"),
 ])
 def test_prefill_shared_row_blocks(orc, rows, h, hk, d, batch, kv_dtype):
