@@ -452,19 +452,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
             for (int r = 0; r < 8; ++r)
                 qo[r] = a.q_bf16 ? (uint32_t)(tr * (DS * 2) + (((2 * r + half) ^ (tr & 15)) * 16))
                                  : (uint32_t)(tr * (DS * 4) + (((4 * (r >> 1) + 2 * half + (r & 1)) ^ (tr & 15)) * 16));
-    #pragma unroll
+#pragma unroll
             for (int pass = 0; pass < 32 / WT_ROWS; ++pass) {
                 if (a.q_bf16) {
                     stage_rows(std::integral_constant<int, 2>{}, pass);
                     if (col / WT_ROWS == pass) {
-    #pragma unroll
+#pragma unroll
                         for (int ks = 0; ks < KSTEPS; ++ks) {
                             const uint4v raw = *reinterpret_cast<const uint4v *>(tile + qo[ks & 7] + (ks >> 3) * 256);
                             if constexpr (BF16) {
                                 qf[ks] = raw;
                             } else {
                                 uint4v cv;
-    #pragma unroll
+#pragma unroll
                                 for (int e = 0; e < 4; ++e) {
                                     const float lo = bf16_bits_to_f32((uint16_t)(raw[e] & 0xffffu)) * q_scale;
                                     const float hi = bf16_bits_to_f32((uint16_t)(raw[e] >> 16)) * q_scale;
@@ -477,7 +477,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
                 } else {
                     stage_rows(std::integral_constant<int, 4>{}, pass);
                     if (col / WT_ROWS == pass) {
-    #pragma unroll
+#pragma unroll
                         for (int ks = 0; ks < KSTEPS; ++ks) {
                             const char *row = tile + (ks >> 2) * 256;
                             const float4v x0 = *reinterpret_cast<const float4v *>(row + qo[2 * (ks & 3)]) * q_scale;
@@ -490,7 +490,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
                             qf[ks] = cv;
                             if constexpr (QSPLIT) {
                                 float rest[8];
-    #pragma unroll
+#pragma unroll
                                 for (int e = 0; e < 4; ++e) {
                                     rest[e] = x0[e] - bf16_bits_to_f32((uint16_t)(cv[e / 2] >> (16 * (e & 1))));
                                     rest[4 + e] = x1[e] - bf16_bits_to_f32((uint16_t)(cv[2 + e / 2] >> (16 * (e & 1))));
@@ -505,7 +505,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
                 }
             }
             if (!row_ok) {
-    #pragma unroll
+#pragma unroll
                 for (int ks = 0; ks < KSTEPS; ++ks) {
                     qf[ks] = uint4v{0u, 0u, 0u, 0u};
                     if constexpr (QSPLIT) qlo[ks] = qf[ks];
@@ -1056,6 +1056,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const char *vt = reinterpret_cast<const char *>(v_lds + buf * STAGE_ELEMS);
 
         float16v s;
+        // mask values of this stage from LDS, requested eight MFMAs before the end of S so
+        // that their latency hides under the matrix work
+        const bool mask_lds_now = HAS_MASK && code == TILE_MASKED && mask_in_lds(st);
+        uint2 mr[4];
+        const char *mb = reinterpret_cast<const char *>(m_lds + (buf * NW + wave) * MI * 64) + col * 16 + 8 * half;
         lds_pipeline<KSTEPS, kLdsAhead, uint4v>(
             [&](int ks) __attribute__((always_inline)) {
                 return *reinterpret_cast<const uint4v *>(kt + k_off[ks & 7] + (ks >> 3) * 256);
@@ -1067,6 +1072,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 } else {
                     if (ks == 0) mfma_f16_vacc_first(s, kf, qf[ks]);
                     else mfma_f16_vacc(s, kf, qf[ks]);
+                }
+                if (HAS_MASK && ks == KSTEPS - 8 && mask_lds_now) {
+#pragma unroll
+                    for (int q4 = 0; q4 < 4; ++q4)
+                        mr[q4] = *reinterpret_cast<const uint2 *>(mb + ((q4 >> 1) * 64 + (q4 & 1) * 32) * 16);
                 }
                 if (nfull) {
                     // instruction n at step n * KSTEPS / NDMA
@@ -1080,12 +1090,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
         // scale and mask (log2 units); this lane holds keys key0 + 8*(r/4) + 4*half + r%4
         if (HAS_MASK && code == TILE_MASKED) {
-            uint2 mr[4];
-            if (mask_in_lds(st)) {
-                const char *mb = reinterpret_cast<const char *>(m_lds + (buf * NW + wave) * MI * 64) + col * 16 + 8 * half;
-#pragma unroll
-                for (int q4 = 0; q4 < 4; ++q4) mr[q4] = *reinterpret_cast<const uint2 *>(mb + ((q4 >> 1) * 64 + (q4 & 1) * 32) * 16);
-            } else {
+            if (!mask_lds_now) {
 #pragma unroll
                 for (int q4 = 0; q4 < 4; ++q4) {
                     const int kf = key0 + 8 * q4 + 4 * half;
@@ -1182,12 +1187,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 }
 
-// One wave classifies one (query block, 64-key tile): TILE_SKIP when every
-// entry is -inf, TILE_OPEN when every entry is zero, else TILE_MASKED.  The
-// pass also clears the status block and the pair counters the attention pass uses.  Only
-// entries of real rows (< rows) and keys (< kv_len) are read.  Grid:
-// (ceil(kv_tiles / 4), row_blocks, batch * blk_heads), four waves per block.
+// One wave classifies TPW consecutive 64-key tiles of one query block: TILE_SKIP
+// when every entry is -inf, TILE_OPEN when every entry is zero, else TILE_MASKED.
+// The pass also clears the status block and the pair counters the attention pass
+// uses.  Only entries of real rows (< rows) and keys (< kv_len) are read.  Grid:
+// (ceil(kv_tiles / (4 * TPW)), row_blocks, batch * blk_heads), four waves per
+// block.  Several tiles per wave keep more bytes in flight per wave when there are
+// waves enough to fill the chip anyway.
+template <int TPW>
 __global__ __launch_bounds__(256) void classify_kernel(PrefillArgs a, uint8_t *blk) {
+    constexpr int kClassifyTiles = TPW;
     if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x < kStatusWords) a.status[threadIdx.x] = 0u;
     if (a.n_pair_cnt > 0) {
         // the pair counters of the attention pass start from zero on every call
@@ -1196,8 +1205,8 @@ __global__ __launch_bounds__(256) void classify_kernel(PrefillArgs a, uint8_t *b
         for (int64_t i = tid; i < a.n_pair_cnt; i += nthreads) a.pair_cnt[i] = 0u;
     }
     const int lane = threadIdx.x & 63;
-    const int kt = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (kt >= a.kv_tiles) return;
+    const int kt0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * kClassifyTiles;
+    if (kt0 >= a.kv_tiles) return;
     const int rb = blockIdx.y;
     const int hg = blockIdx.z % a.blk_heads;
     const int b = blockIdx.z / a.blk_heads;
@@ -1205,67 +1214,107 @@ __global__ __launch_bounds__(256) void classify_kernel(PrefillArgs a, uint8_t *b
     const int h0 = hg * a.heads_per_wg;
     const uint16_t *mbase = (const uint16_t *)a.mask + b * a.m_bs;
     const uint16_t neg_inf = a.mask_bf16 ? 0xFF80u : 0xFC00u;
-    const int key0 = kt * kTile;
-    bool any_visible = false, any_nonzero = false;
-    auto see = [&](uint16_t m16) {
-        any_visible |= m16 != neg_inf;
-        any_nonzero |= (m16 & 0x7fffu) != 0;
+    uint8_t *out = blk + (((int64_t)b * a.blk_heads + hg) * a.row_blocks + rb) * a.blk_stride;
+    auto code_of = [&](bool any_visible, bool any_nonzero) -> uint8_t {
+        const bool vis = __ballot(any_visible) != 0;
+        const bool nz = __ballot(any_nonzero) != 0;
+        return !vis ? TILE_SKIP : (nz ? TILE_MASKED : TILE_OPEN);
     };
-    if (a.mask_dma && key0 + kTile <= a.kv_len) {
-        // 8 lanes per 64-key row, 8 keys (16 bytes) per lane, 8 rows per load; the 8 loads
-        // of 64 rows are requested before any is looked at (addresses clamped to existing
-        // rows, the copies not counted), so they share one memory round trip
-        const int k8 = key0 + 8 * (lane & 7);
-        constexpr int U = 8;
-        for (int s0 = 0; s0 < slots; s0 += 8 * U) {
-            uint4v raw[U];
+    if (a.mask_dma && slots <= 64 && (kt0 + kClassifyTiles) * kTile <= a.kv_len) {
+        // all tiles full, at most 64 rows: 8 lanes per 64-key row (8 keys, 16 bytes each),
+        // 8 rows per load; the loads of every tile are requested before any is looked at
+        const int k8 = 8 * (lane & 7);
+        uint4v raw[kClassifyTiles][8];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int s = min(s0 + 8 * u + (lane >> 3), slots - 1);
-                const int head = h0 + s / a.rows_per_wg;
-                const int row = min(rb * a.rows_per_wg + s % a.rows_per_wg, a.rows - 1);
-                raw[u] = *reinterpret_cast<const uint4v *>(mbase + head * a.m_hs + (int64_t)row * a.m_rs + k8);
+        for (int u = 0; u < 8; ++u) {
+            if (8 * u < slots) {
+                const int s_ = min(8 * u + (lane >> 3), slots - 1);
+                const int head = h0 + s_ / a.rows_per_wg;
+                const int row = min(rb * a.rows_per_wg + s_ % a.rows_per_wg, a.rows - 1);
+                const uint16_t *src = mbase + head * a.m_hs + (int64_t)row * a.m_rs + kt0 * kTile + k8;
+#pragma unroll
+                for (int t = 0; t < kClassifyTiles; ++t) raw[t][u] = *reinterpret_cast<const uint4v *>(src + t * kTile);
             }
+        }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int s = s0 + 8 * u + (lane >> 3);
-                if (s < slots && rb * a.rows_per_wg + s % a.rows_per_wg < a.rows) {
+        for (int t = 0; t < kClassifyTiles; ++t) {
+            bool any_visible = false, any_nonzero = false;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int s_ = 8 * u + (lane >> 3);
+                if (8 * u < slots && s_ < slots && rb * a.rows_per_wg + s_ % a.rows_per_wg < a.rows) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        see((uint16_t)(raw[u][e] & 0xffffu));
-                        see((uint16_t)(raw[u][e] >> 16));
+                        const uint16_t lo = (uint16_t)(raw[t][u][e] & 0xffffu), hi = (uint16_t)(raw[t][u][e] >> 16);
+                        any_visible |= lo != neg_inf || hi != neg_inf;
+                        any_nonzero |= ((lo | hi) & 0x7fffu) != 0;
+                    }
+                }
+            }
+            const uint8_t code = code_of(any_visible, any_nonzero);
+            if (lane == 0) out[kt0 + t] = code;
+        }
+        return;
+    }
+    for (int kt = kt0; kt < kt0 + kClassifyTiles && kt < a.kv_tiles; ++kt) {
+        const int key0 = kt * kTile;
+        bool any_visible = false, any_nonzero = false;
+        auto see = [&](uint16_t m16) {
+            any_visible |= m16 != neg_inf;
+            any_nonzero |= (m16 & 0x7fffu) != 0;
+        };
+        if (a.mask_dma && key0 + kTile <= a.kv_len) {
+            // 8 lanes per 64-key row, 8 keys (16 bytes) per lane, 8 rows per load; the 8 loads
+            // of 64 rows are requested before any is looked at (addresses clamped to existing
+            // rows, the copies not counted), so they share one memory round trip
+            const int k8 = key0 + 8 * (lane & 7);
+            constexpr int U = 8;
+            for (int s0 = 0; s0 < slots; s0 += 8 * U) {
+                uint4v raw[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int s = min(s0 + 8 * u + (lane >> 3), slots - 1);
+                    const int head = h0 + s / a.rows_per_wg;
+                    const int row = min(rb * a.rows_per_wg + s % a.rows_per_wg, a.rows - 1);
+                    raw[u] = *reinterpret_cast<const uint4v *>(mbase + head * a.m_hs + (int64_t)row * a.m_rs + k8);
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int s = s0 + 8 * u + (lane >> 3);
+                    if (s < slots && rb * a.rows_per_wg + s % a.rows_per_wg < a.rows) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            see((uint16_t)(raw[u][e] & 0xffffu));
+                            see((uint16_t)(raw[u][e] >> 16));
+                        }
+                    }
+                }
+            }
+        } else {
+            // any alignment, or the ragged last tile: one key per lane; 32 rows are requested
+            // before any is looked at (clamped to existing rows; the copies are not counted)
+            const int key = key0 + lane;
+            if (key < a.kv_len) {
+                constexpr int U = 32;
+                for (int s0 = 0; s0 < slots; s0 += U) {
+                    uint16_t v[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int s = min(s0 + u, slots - 1);
+                        const int head = h0 + s / a.rows_per_wg;
+                        const int row = min(rb * a.rows_per_wg + s % a.rows_per_wg, a.rows - 1);
+                        v[u] = mbase[head * a.m_hs + (int64_t)row * a.m_rs + key];
+                    }
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int s = s0 + u;
+                        if (s < slots && rb * a.rows_per_wg + s % a.rows_per_wg < a.rows) see(v[u]);
                     }
                 }
             }
         }
-    } else {
-        // any alignment, or the ragged last tile: one key per lane; 32 rows are requested
-        // before any is looked at (clamped to existing rows; the copies are not counted)
-        const int key = key0 + lane;
-        if (key < a.kv_len) {
-            constexpr int U = 32;
-            for (int s0 = 0; s0 < slots; s0 += U) {
-                uint16_t v[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int s = min(s0 + u, slots - 1);
-                    const int head = h0 + s / a.rows_per_wg;
-                    const int row = min(rb * a.rows_per_wg + s % a.rows_per_wg, a.rows - 1);
-                    v[u] = mbase[head * a.m_hs + (int64_t)row * a.m_rs + key];
-                }
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int s = s0 + u;
-                    if (s < slots && rb * a.rows_per_wg + s % a.rows_per_wg < a.rows) see(v[u]);
-                }
-            }
-        }
-    }
-    const bool vis = __ballot(any_visible) != 0;
-    const bool nz = __ballot(any_nonzero) != 0;
-    if (lane == 0) {
-        uint8_t *out = blk + (((int64_t)b * a.blk_heads + hg) * a.row_blocks + rb) * a.blk_stride;
-        out[kt] = !vis ? TILE_SKIP : (nz ? TILE_MASKED : TILE_OPEN);
+        const uint8_t code = code_of(any_visible, any_nonzero);
+        if (lane == 0) out[kt] = code;
     }
 }
 
@@ -1557,8 +1606,15 @@ hipError_t launch_prefill(const attn_prefill_params *p, const PrefillPlan *plan,
     a.score_scale = p->scale * kLog2e;
 
     if (a.mask) {
-        dim3 grid((plan->kv_tiles + 3) / 4, plan->row_blocks, p->batch * a.blk_heads);
-        hipLaunchKernelGGL(classify_kernel, grid, dim3(256), 0, stream, a, (uint8_t *)a.blk);
+        // four tiles per wave once that still leaves 4096 waves or more
+        const int64_t units = (int64_t)plan->kv_tiles * plan->row_blocks * p->batch * a.blk_heads;
+        if (units >= 4 * 4096) {
+            dim3 grid((plan->kv_tiles + 15) / 16, plan->row_blocks, p->batch * a.blk_heads);
+            hipLaunchKernelGGL(classify_kernel<4>, grid, dim3(256), 0, stream, a, (uint8_t *)a.blk);
+        } else {
+            dim3 grid((plan->kv_tiles + 3) / 4, plan->row_blocks, p->batch * a.blk_heads);
+            hipLaunchKernelGGL(classify_kernel<1>, grid, dim3(256), 0, stream, a, (uint8_t *)a.blk);
+        }
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }

@@ -75,7 +75,7 @@ TRAFFIC_ROWS = {
                             "attention_flash_attn_03_amd/csrc/device_common.h",
                             "attention_flash_attn_03_amd/csrc/internal.h"]},
     "causal2k": {"file": "prefill_causal2k_traffic.json",
-                 "kernels": {"classify": "classify_kernel", "attention": "prefill_kernel"},
+                 "kernels": {"classify": "classify_kernel", "attention": "narrow_kernel"},
                  "sources": ["attention_flash_attn_03_amd/csrc/prefill.hip",
                              "attention_flash_attn_03_amd/csrc/device_common.h",
                              "attention_flash_attn_03_amd/csrc/internal.h"]},
