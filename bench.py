@@ -72,11 +72,14 @@ TRAFFIC_ROWS = {
     "prefill": {"file": "prefill_chunked8k_traffic.json",
                 "kernels": {"classify": "classify_kernel", "attention": "wide_kernel"},
                 "sources": ["attention_flash_attn_03_amd/csrc/prefill.hip",
+                            "attention_flash_attn_03_amd/csrc/prefill_common.h",
                             "attention_flash_attn_03_amd/csrc/device_common.h",
                             "attention_flash_attn_03_amd/csrc/internal.h"]},
     "causal2k": {"file": "prefill_causal2k_traffic.json",
                  "kernels": {"classify": "classify_kernel", "attention": "narrow_kernel"},
                  "sources": ["attention_flash_attn_03_amd/csrc/prefill.hip",
+                             "attention_flash_attn_03_amd/csrc/narrow.hip",
+                             "attention_flash_attn_03_amd/csrc/prefill_common.h",
                              "attention_flash_attn_03_amd/csrc/device_common.h",
                              "attention_flash_attn_03_amd/csrc/internal.h"]},
 }
