@@ -1,8 +1,9 @@
 """GPU parity of attn_paged_decode against the fp64 oracle, elementwise within
 |err| <= 2e-3 * (1 + |ref|): oracle-sized page tables, bf16 and head_dim 256,
 empty contexts, NaN-poisoned unused slots, the interleaved K/V token record,
-paged == contiguous (through attn_prefill), the same logical KV under two
-different physical page placements (bit-identical), and the full-size
+paged == contiguous (through attn_prefill, within a bound derived from the f16
+rounding of P), the same logical KV under two different physical page
+placements (bit-identical), and the full-size
 paged-decode configuration (64 sequences, contexts 512..16384, 65536-page
 pool), every sequence, in the benchmark's launch configuration."""
 import math
@@ -83,10 +84,29 @@ def test_interleaved_token_record(orc):
     assert_close(got, _oracle(orc, case), "interleaved")
 
 
+def _p_rounding_bound(orc, q, kk, vv, o, scale):
+    """Largest |O_a - O_b| between two kernels that both round Q and K/V to the same f16
+    values, round every probability p to f16 and divide by the sum of the rounded p,
+    but against different running maxima and in different f32 orders.  For one kernel,
+    with weights w_j = p_j / l and n keys:
+      f16 rounding of p above 2^-14 (relative 2^-11):  2^-11 sum_j w_j |v_j - O|
+      below 2^-14 (absolute 2^-25, and l >= 1):         n 2^-25 max_j |v_j - O|
+      f32 accumulation of sum p v and of l:             2 n 2^-24 sum_j w_j (|v_j| + |O|)
+    with |v_j - O| <= |v_j| + |O| and sum_j w_j |v_j| the attention of |V|, taken from
+    the oracle.  Two kernels: twice that."""
+    n = kk.shape[1]
+    a = orc.attention(q, kk, np.abs(vv), scale=scale)
+    ao = np.abs(o)
+    vmax = float(np.max(np.abs(vv)))
+    one = 2.0 ** -11 * (a + ao) + n * 2.0 ** -25 * (vmax + ao) + 2 * n * 2.0 ** -24 * (a + ao)
+    return 2 * one
+
+
 def test_paged_equals_contiguous_prefill(orc):
     """The same logical KV through the page table (decode kernel) and as one
     contiguous range (prefill kernel): both match the oracle, and each other
-    within the same bound (the kernels round Q and P in different blockings)."""
+    within the bound that their f16 rounding of the probabilities against
+    different running maxima allows (about half the oracle bound here)."""
     announce("decode paged vs contiguous prefill")
     case = workloads.paged_case(batch=3, ctx_lo=200, ctx_hi=600, num_pages=200, n_heads=8, n_kv_heads=2,
                                 head_dim=128, seed=38)
@@ -103,7 +123,10 @@ def test_paged_equals_contiguous_prefill(orc):
         torch.cuda.synchronize()
         contiguous = out.cpu().numpy()[0, 0].astype(np.float64)
         assert_close(contiguous, ref[b], "contiguous")
-        assert_close(paged[b], contiguous, "paged vs contiguous")
+        bound = _p_rounding_bound(orc, case.q[b][None, None], kk, vv, ref[b][None, None], case.scale)[0, 0]
+        d = np.abs(paged[b] - contiguous)
+        assert np.all(d <= bound), "paged vs contiguous: |d| %g above the rounding bound %g" % (
+            float(d.max()), float(bound.flat[np.argmax(d - bound)]))
 
 
 def relocate_pages(case, seed):

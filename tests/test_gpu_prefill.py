@@ -218,6 +218,23 @@ def test_gqa_matches_repeated_kv(orc):
     assert_close(mha, _oracle(orc, rep), "mha")
 
 
+def test_gqa_matches_repeated_kv_bitwise(orc):
+    """Unmasked, with neither KV splits nor row-block pairing in either launch: every query
+    column then sees the same stages in the same order under either head mapping, and its
+    scores, softmax and P V do not depend on the other columns of its tile, so GQA and the
+    repeated-KV MHA call agree bit for bit."""
+    announce("prefill GQA vs repeated KV, bitwise (unmasked, 1024 x 1024, 16/4 heads, d 128)")
+    case = workloads.prefill_synthetic("t", rows=1024, kv_len=1024, cached=0, n_heads=16, n_kv_heads=4,
+                                       head_dim=128, seed=23, q_std=1 / math.sqrt(128), kv_std=1.0)
+    gqa = _run(case, mask=False)
+    rep = workloads.PrefillCase("rep", case.q, np.repeat(case.k, 4, axis=2), np.repeat(case.v, 4, axis=2),
+                                case.mask, case.scale, case.kv_len)
+    mha = _run(rep, mask=False)
+    assert np.array_equal(gqa, mha), "GQA and repeated-KV MHA differ: max |d| %g" % float(np.max(np.abs(gqa - mha)))
+    rows = np.arange(0, 1024, 37)
+    assert_close(gqa[:, rows], _oracle(orc, case, rows=rows, mask=False), "gqa unmasked")
+
+
 def _rows_per_block(rows, block, per, seed):
     """`per` distinct rows from every block of `block` consecutive rows (first and last included)."""
     rng = np.random.Generator(np.random.PCG64(seed))
