@@ -1214,6 +1214,11 @@ __global__ __launch_bounds__(256) void classify_kernel(PrefillArgs a, uint8_t *b
     const int h0 = hg * a.heads_per_wg;
     const uint16_t *mbase = (const uint16_t *)a.mask + b * a.m_bs;
     const uint16_t neg_inf = a.mask_bf16 ? 0xFF80u : 0xFC00u;
+    // rows_per_wg is a power of two: a slot's (head, row) by shift and mask, not by division
+    const int rsh = __builtin_ctz(a.rows_per_wg), rmask = a.rows_per_wg - 1;
+    // every mask element of a batch item within 2^31 bytes of its first: 32-bit buffer offsets
+    const bool off32 = ((int64_t)(a.n_heads - 1) * a.m_hs + (int64_t)(a.rows - 1) * a.m_rs + a.kv_len) * 2 <
+                       ((int64_t)1 << 31);
     uint8_t *out = blk + (((int64_t)b * a.blk_heads + hg) * a.row_blocks + rb) * a.blk_stride;
     auto code_of = [&](bool any_visible, bool any_nonzero) -> uint8_t {
         const bool vis = __ballot(any_visible) != 0;
@@ -1229,8 +1234,8 @@ __global__ __launch_bounds__(256) void classify_kernel(PrefillArgs a, uint8_t *b
         for (int u = 0; u < 8; ++u) {
             if (8 * u < slots) {
                 const int s_ = min(8 * u + (lane >> 3), slots - 1);
-                const int head = h0 + s_ / a.rows_per_wg;
-                const int row = min(rb * a.rows_per_wg + s_ % a.rows_per_wg, a.rows - 1);
+                const int head = h0 + (s_ >> rsh);
+                const int row = min(rb * a.rows_per_wg + (s_ & rmask), a.rows - 1);
                 const uint16_t *src = mbase + head * a.m_hs + (int64_t)row * a.m_rs + kt0 * kTile + k8;
 #pragma unroll
                 for (int t = 0; t < kClassifyTiles; ++t) raw[t][u] = *reinterpret_cast<const uint4v *>(src + t * kTile);
@@ -1242,7 +1247,7 @@ __global__ __launch_bounds__(256) void classify_kernel(PrefillArgs a, uint8_t *b
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 const int s_ = 8 * u + (lane >> 3);
-                if (8 * u < slots && s_ < slots && rb * a.rows_per_wg + s_ % a.rows_per_wg < a.rows) {
+                if (8 * u < slots && s_ < slots && rb * a.rows_per_wg + (s_ & rmask) < a.rows) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const uint16_t lo = (uint16_t)(raw[t][u][e] & 0xffffu), hi = (uint16_t)(raw[t][u][e] >> 16);
@@ -1274,14 +1279,14 @@ __global__ __launch_bounds__(256) void classify_kernel(PrefillArgs a, uint8_t *b
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int s = min(s0 + 8 * u + (lane >> 3), slots - 1);
-                    const int head = h0 + s / a.rows_per_wg;
-                    const int row = min(rb * a.rows_per_wg + s % a.rows_per_wg, a.rows - 1);
+                    const int head = h0 + (s >> rsh);
+                    const int row = min(rb * a.rows_per_wg + (s & rmask), a.rows - 1);
                     raw[u] = *reinterpret_cast<const uint4v *>(mbase + head * a.m_hs + (int64_t)row * a.m_rs + k8);
                 }
 #pragma unroll
                 for (int u = 0; u < U; ++u) {
                     const int s = s0 + 8 * u + (lane >> 3);
-                    if (s < slots && rb * a.rows_per_wg + s % a.rows_per_wg < a.rows) {
+                    if (s < slots && rb * a.rows_per_wg + (s & rmask) < a.rows) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             see((uint16_t)(raw[u][e] & 0xffffu));
@@ -1291,27 +1296,58 @@ __global__ __launch_bounds__(256) void classify_kernel(PrefillArgs a, uint8_t *b
                 }
             }
         } else {
-            // any alignment, or the ragged last tile: one key per lane; 32 rows are requested
-            // before any is looked at (clamped to existing rows; the copies are not counted)
+            // any alignment, or the ragged last tile: one key per lane; 64 rows (32 with 64-bit
+            // offsets) are requested before any is looked at.  Keys past kv_len load key kv_len - 1 and slots past the
+            // row block load clamped rows: elements of this same tile that are counted anyway,
+            // so the ORs below are unchanged and no element needs excluding.  Every lane stays
+            // active: the slots' row offsets are computed one per lane, then taken lane by lane
+            // as the scalar offset of a buffer load.
             const int key = key0 + lane;
-            if (key < a.kv_len) {
+            const int key_c = key < a.kv_len ? key : a.kv_len - 1;
+            uint32_t acc_x = 0u, acc_n = 0u;  // OR of (m ^ -inf) and of m over this lane's elements
+            if (off32) {
+                constexpr int U = 64;
+                const __amdgpu_buffer_rsrc_t rsrc =
+                    __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(mbase), 0, 0x7fffffff, kRawBufferFlags);
+                for (int s0 = 0; s0 < slots; s0 += U) {
+                    const int sl = min(s0 + (lane & (U - 1)), slots - 1);
+                    const uint32_t my_off =
+                        (uint32_t)(((int64_t)(h0 + (sl >> rsh)) * a.m_hs +
+                                    (int64_t)min(rb * a.rows_per_wg + (sl & rmask), a.rows - 1) * a.m_rs) *
+                                   2);
+                    uint16_t v[U];
+#pragma unroll
+                    for (int u = 0; u < U; ++u)
+                        v[u] = __builtin_amdgcn_raw_buffer_load_b16(rsrc, key_c * 2, __builtin_amdgcn_readlane(my_off, u), 0);
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        acc_x |= (uint32_t)(v[u] ^ neg_inf);
+                        acc_n |= v[u];
+                    }
+                }
+            } else {
                 constexpr int U = 32;
                 for (int s0 = 0; s0 < slots; s0 += U) {
+                    const int sl = min(s0 + (lane & (U - 1)), slots - 1);
+                    const int64_t my_off = (int64_t)(h0 + (sl >> rsh)) * a.m_hs +
+                                           (int64_t)min(rb * a.rows_per_wg + (sl & rmask), a.rows - 1) * a.m_rs;
+                    const uint32_t off_lo = (uint32_t)my_off, off_hi = (uint32_t)((uint64_t)my_off >> 32);
                     uint16_t v[U];
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
-                        const int s = min(s0 + u, slots - 1);
-                        const int head = h0 + s / a.rows_per_wg;
-                        const int row = min(rb * a.rows_per_wg + s % a.rows_per_wg, a.rows - 1);
-                        v[u] = mbase[head * a.m_hs + (int64_t)row * a.m_rs + key];
+                        const uint64_t off_u = (uint64_t)__builtin_amdgcn_readlane(off_lo, u) |
+                                               ((uint64_t)__builtin_amdgcn_readlane(off_hi, u) << 32);
+                        v[u] = (mbase + off_u)[key_c];
                     }
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
-                        const int s = s0 + u;
-                        if (s < slots && rb * a.rows_per_wg + s % a.rows_per_wg < a.rows) see(v[u]);
+                        acc_x |= (uint32_t)(v[u] ^ neg_inf);
+                        acc_n |= v[u];
                     }
                 }
             }
+            any_visible = acc_x != 0u;
+            any_nonzero = (acc_n & 0x7fffu) != 0u;
         }
         const uint8_t code = code_of(any_visible, any_nonzero);
         if (lane == 0) out[kt] = code;

@@ -235,6 +235,37 @@ def test_gqa_matches_repeated_kv_bitwise(orc):
     assert_close(gqa[:, rows], _oracle(orc, case, rows=rows, mask=False), "gqa unmasked")
 
 
+def test_mask_heads_more_than_2gib_apart(orc):
+    """A per-head f16 mask whose two heads lie 2 GiB apart (a strided view of one allocation)
+    and whose rows have an odd key count: the tile classification reads it one key per lane
+    with 64-bit offsets, and the attention kernel reads its masked tiles element by element.
+    Every row is compared with the oracle."""
+    announce("prefill per-head mask, heads 2 GiB apart (96 x 301, 2/1 heads, d 128)")
+    kw = dict(rows=96, kv_len=301, cached=205, n_heads=2, n_kv_heads=1, head_dim=128,
+              q_std=1 / math.sqrt(128), kv_std=1.0, holes=0.1)
+    case = workloads.prefill_synthetic("t", seed=24, **kw)
+    other = workloads.prefill_synthetic("t", seed=25, **kw)  # head 1: the same frontier, other holes
+    mask = np.concatenate([case.mask, other.mask], axis=1)   # [1, 2, 96, 301] f16
+    gap = 1 << 30                                             # elements between the heads: 2 GiB
+    n = 96 * 301
+    big = torch.empty((gap + n,), dtype=torch.float16, device="cuda")
+    big[:n] = torch.from_numpy(np.ascontiguousarray(mask[0, 0]).reshape(-1)).cuda()
+    big[gap:gap + n] = torch.from_numpy(np.ascontiguousarray(mask[0, 1]).reshape(-1)).cuda()
+    m = big.as_strided((1, 2, 96, 301), (0, gap, 301, 1))
+    q, k, v = dev(case.q), dev(case.k), dev(case.v)
+    out = torch.full(case.q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    p = fa.prefill_params(q, k, v, m, out, scale=case.scale)
+    ws = torch.full((fa.prefill_workspace_bytes(p),), 0xA5, dtype=torch.uint8, device="cuda")
+    fa.attn_prefill(q, k, v, m, out, scale=case.scale, workspace=ws)
+    torch.cuda.synchronize()
+    flags, _ = fa.prefill_status(ws)
+    assert flags == 0, "status block flags 0x%x after the call" % flags
+    got = out.cpu().numpy()
+    del big, m
+    ref = orc.attention(case.q, case.k, case.v, mask, scale=case.scale)
+    assert_close(got, ref, "heads 2 GiB apart")
+
+
 def _rows_per_block(rows, block, per, seed):
     """`per` distinct rows from every block of `block` consecutive rows (first and last included)."""
     rng = np.random.Generator(np.random.PCG64(seed))
