@@ -55,22 +55,30 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepareArgs a) {
     const int slot = (int)(item % slots);
     const int t = (int)((item / slots) % a.max_tokens);
     const int b = (int)(item / ((int64_t)slots * a.max_tokens));
-    int n = a.query_lens[b];
-    n = n < 0 ? 0 : (n > a.max_tokens ? a.max_tokens : n);
-    if (t >= n) return;
-    int st = a.position_starts[b];
-    st = st < 0 ? 0 : st;
-    const int64_t pos64 = (int64_t)st + t;
     const bool is_q = slot < a.n_heads, is_k = !is_q && slot < a.n_heads + a.n_kv_heads;
     const int head = is_q ? slot : (is_k ? slot - a.n_heads : slot - a.n_heads - a.n_kv_heads);
-    if (!is_q && pos64 >= a.ctx_cap) return;  // past the pages this sequence may use
-
+    // Every load that does not depend on another is issued before any is used (one memory
+    // round trip): the sequence's query length and start, the head's features (row t exists
+    // for every t < max_tokens) and its norm weights.  Only the page entry waits for the start.
+    const int n_raw = a.query_lens[b];
+    const int st_raw = a.position_starts[b];
     const float *src = is_q ? a.q_raw + b * a.qr_bs + (int64_t)t * a.qr_ts + (int64_t)head * a.qr_hs
                             : (is_k ? a.k_raw + b * a.kr_bs + (int64_t)t * a.kr_ts + (int64_t)head * a.kr_hs
                                     : a.v_raw + b * a.vr_bs + (int64_t)t * a.vr_ts + (int64_t)head * a.vr_hs);
     float x[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) x[k] = src[lane + 64 * k];
+    float wn[PER];
+    if ((is_q || is_k) && a.use_norm) {
+        const float *w = is_q ? a.q_norm + (int64_t)head * a.qn_hs : a.k_norm + (int64_t)head * a.kn_hs;
+#pragma unroll
+        for (int k = 0; k < PER; ++k) wn[k] = w[lane + 64 * k];
+    }
+    const int n = n_raw < 0 ? 0 : (n_raw > a.max_tokens ? a.max_tokens : n_raw);
+    if (t >= n) return;
+    const int st = st_raw < 0 ? 0 : st_raw;
+    const int64_t pos64 = (int64_t)st + t;
+    if (!is_q && pos64 >= a.ctx_cap) return;  // past the pages this sequence may use
 
     if (is_q || is_k) {
         if (a.use_norm) {
@@ -80,9 +88,8 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepareArgs a) {
 #pragma unroll
             for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
             const float inv = 1.f / sqrtf(ss / (float)D + a.eps);
-            const float *w = is_q ? a.q_norm + (int64_t)head * a.qn_hs : a.k_norm + (int64_t)head * a.kn_hs;
 #pragma unroll
-            for (int k = 0; k < PER; ++k) x[k] = x[k] * inv * w[lane + 64 * k];
+            for (int k = 0; k < PER; ++k) x[k] = x[k] * inv * wn[k];
         }
         // rotary embedding: the partner of feature d comes from LDS
 #pragma unroll
