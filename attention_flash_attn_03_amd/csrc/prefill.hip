@@ -127,113 +127,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(1, 1)))
         const int bh = a.blk_heads == 1 ? 0 : hg;
         return (const_u32 *)(a.blk + (((int64_t)b * a.blk_heads + bh) * a.row_blocks + rbx) * a.blk_stride);
     };
-    // Stages of a row block that are not skipped, and the stage after the first `cut`
-    // of them: the row of tile codes is scanned by the whole wave, one dword (four
-    // codes) per lane, with a wave-wide sum or prefix sum.
-    auto lane_stages = [&](const uint8_t *row, int w) -> int {  // unskipped stages in dword w
-        int n = 0;
-        if (w < a.blk_stride / 4) {
-            const uint32_t word = reinterpret_cast<const uint32_t *>(row)[w];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = 4 * w + j;
-                if (t < a.kv_tiles && ((word >> (8 * j)) & 0xffu) != TILE_SKIP) n += min(SPT, n_stages - t * SPT);
-            }
-        }
-        return n;
-    };
-    auto code_bytes = [&](int rbx) -> const uint8_t * {
-        const int bh = a.blk_heads == 1 ? 0 : hg;
-        return a.blk + (((int64_t)b * a.blk_heads + bh) * a.row_blocks + rbx) * a.blk_stride;
-    };
-    auto count_stages = [&](int rbx) -> int {
-        const uint8_t *row = code_bytes(rbx);
-        int n = 0;
-        for (int w0 = 0; w0 < a.blk_stride / 4; w0 += 64) n += lane_stages(row, w0 + lane);
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) n += __shfl_xor(n, off);
-        return __builtin_amdgcn_readfirstlane(n);
-    };
-    auto stage_after = [&](int rbx, int cut) -> int {
-        const uint8_t *row = code_bytes(rbx);
-        int before = 0;  // unskipped stages in earlier passes
-        for (int w0 = 0; w0 < a.blk_stride / 4; w0 += 64) {
-            const int w = w0 + lane;
-            const int mine = lane_stages(row, w);
-            int incl = mine;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int up = __shfl_up(incl, off);
-                if (lane >= off) incl += up;
-            }
-            const uint64_t hit = __ballot(before + incl >= cut);
-            if (hit) {
-                const int L = __builtin_ctzll(hit);
-                // in lane L: walk its four tiles from the count before it
-                int n = before + incl - mine, at = n_stages;
-                if (lane == L) {
-                    const uint32_t word = reinterpret_cast<const uint32_t *>(row)[w];
-                    for (int j = 0; j < 4; ++j) {
-                        const int t = 4 * w + j;
-                        if (t < a.kv_tiles && ((word >> (8 * j)) & 0xffu) != TILE_SKIP) {
-                            const int k = min(SPT, n_stages - t * SPT);
-                            if (n + k >= cut) {
-                                at = t * SPT + (cut - n);
-                                break;
-                            }
-                            n += k;
-                        }
-                    }
-                }
-                return __builtin_amdgcn_readfirstlane(__shfl(at, L));
-            }
-            before += __shfl(incl, 63);
-        }
-        return n_stages;
-    };
-
-    // The tasks of this workgroup: a row block and a stage range each.  Without
-    // pairing it is one row block (the last ones first: a causal frontier makes them
-    // the heaviest).  With pairing, row blocks lo = p and hi = RB-1-p share two
-    // workgroups: side 0 takes the first half of their unskipped stages from hi,
-    // side 1 the rest of hi and then all of lo, so both sides carry the same load
-    // whatever the mask; when hi is cut, the side that finishes it second merges the
-    // two partial results.
-    int rb0 = a.row_blocks - 1 - idx, beg0 = split_begin, end0 = split_end, side0 = -1;
-    int rb1 = 0, beg1 = 0, end1 = 0, ntask = 1, pair = 0;
-    if constexpr (HAS_MASK) {
-        if (a.pairing) {
-            const int npairs = a.row_blocks >> 1;
-            if (idx < 2 * npairs) {
-                pair = idx >> 1;
-                const int side = idx & 1;
-                const int rb_lo = pair, rb_hi = a.row_blocks - 1 - pair;
-                const int w_hi = count_stages(rb_hi);
-                const int w_lo = count_stages(rb_lo);
-                const int cut = min((w_hi + w_lo + 1) >> 1, w_hi);
-                const bool shared = cut > 0 && cut < w_hi;
-                const int s_cut = shared ? stage_after(rb_hi, cut) : n_stages;
-                beg0 = 0;
-                end0 = n_stages;
-                if (side == 0) {
-                    rb0 = rb_hi;
-                    end0 = s_cut;
-                    side0 = shared ? 0 : -1;
-                } else if (shared) {
-                    rb0 = rb_hi;
-                    beg0 = s_cut;
-                    side0 = 1;
-                    rb1 = rb_lo;
-                    end1 = n_stages;
-                    ntask = 2;
-                } else {
-                    rb0 = rb_lo;
-                }
-            } else {
-                rb0 = npairs;  // the middle row block of an odd count
-            }
-        }
-    }
+    // the tasks of this workgroup (row blocks and stage ranges; pairing of heavy and light
+    // row blocks with a cut in the heavy one)
+    const PrefillTasks tasks = prefill_tasks<SPT, HAS_MASK>(a, b, hg, idx, split_begin, split_end, n_stages, lane);
+    const int rb0 = tasks.rb0, beg0 = tasks.beg0, end0 = tasks.end0, side0 = tasks.side0;
+    const int rb1 = tasks.rb1, beg1 = tasks.beg1, end1 = tasks.end1, ntask = tasks.ntask, pair = tasks.pair;
 
     for (int task = 0; task < ntask; ++task) {
     const int rb = task == 0 ? rb0 : rb1;

@@ -140,6 +140,131 @@ __device__ __forceinline__ uint4v read_tr16_pair(const uint16_t *p0, const uint1
 // Row strides (elements) below this keep every offset inside a 64-row stage under 2^32 bytes.
 constexpr int64_t kOff32Stride = (int64_t)1 << 25;
 
+// One row of tile codes (a row block's byte per 64-key tile, padded to whole dwords),
+// as the classify pass wrote it: its stages that are not skipped (SPT stages per tile
+// code, the last tile possibly fewer), and the stage after the first `cut` of them.
+// The whole wave scans the row, one dword (four codes) per lane, with a wave-wide sum
+// or prefix sum; every lane gets the result.
+template <int SPT>
+struct CodeRow {
+    const uint8_t *row;
+    int stride, kv_tiles, n_stages;
+
+    __device__ __forceinline__ int lane_stages(int w) const {  // unskipped stages in dword w
+        int n = 0;
+        if (w < stride / 4) {
+            const uint32_t word = reinterpret_cast<const uint32_t *>(row)[w];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = 4 * w + j;
+                if (t < kv_tiles && ((word >> (8 * j)) & 0xffu) != TILE_SKIP) n += min(SPT, n_stages - t * SPT);
+            }
+        }
+        return n;
+    }
+    __device__ __forceinline__ int count(int lane) const {
+        int n = 0;
+        for (int w0 = 0; w0 < stride / 4; w0 += 64) n += lane_stages(w0 + lane);
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) n += __shfl_xor(n, off);
+        return __builtin_amdgcn_readfirstlane(n);
+    }
+    __device__ __forceinline__ int stage_after(int cut, int lane) const {
+        int before = 0;  // unskipped stages in earlier passes
+        for (int w0 = 0; w0 < stride / 4; w0 += 64) {
+            const int w = w0 + lane;
+            const int mine = lane_stages(w);
+            int incl = mine;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int up = __shfl_up(incl, off);
+                if (lane >= off) incl += up;
+            }
+            const uint64_t hit = __ballot(before + incl >= cut);
+            if (hit) {
+                const int L = __builtin_ctzll(hit);
+                // in lane L: walk its four tiles from the count before it
+                int n = before + incl - mine, at = n_stages;
+                if (lane == L) {
+                    const uint32_t word = reinterpret_cast<const uint32_t *>(row)[w];
+                    for (int j = 0; j < 4; ++j) {
+                        const int t = 4 * w + j;
+                        if (t < kv_tiles && ((word >> (8 * j)) & 0xffu) != TILE_SKIP) {
+                            const int k = min(SPT, n_stages - t * SPT);
+                            if (n + k >= cut) {
+                                at = t * SPT + (cut - n);
+                                break;
+                            }
+                            n += k;
+                        }
+                    }
+                }
+                return __builtin_amdgcn_readfirstlane(__shfl(at, L));
+            }
+            before += __shfl(incl, 63);
+        }
+        return n_stages;
+    }
+};
+
+// The tasks of workgroup (b, hg, idx): a row block and a stage range each.  Without
+// pairing it is one row block (the last ones first: a causal frontier makes them the
+// heaviest) over the workgroup's KV split.  With pairing, row blocks lo = p and
+// hi = RB-1-p share two workgroups: side 0 takes the first half of their unskipped
+// stages from hi, side 1 the rest of hi and then all of lo, so both sides carry the
+// same load whatever the mask; when hi is cut, the side that finishes it second
+// merges the two partial results (side0 says which side of a cut block task 0 is,
+// -1 when it is not cut).
+struct PrefillTasks {
+    int rb0, beg0, end0, side0;
+    int rb1, beg1, end1;
+    int ntask, pair;
+};
+template <int SPT, bool HAS_MASK>
+__device__ __forceinline__ PrefillTasks prefill_tasks(const PrefillArgs &a, int b, int hg, int idx, int split_begin,
+                                                      int split_end, int n_stages, int lane) {
+    PrefillTasks t{a.row_blocks - 1 - idx, split_begin, split_end, -1, 0, 0, 0, 1, 0};
+    if constexpr (HAS_MASK) {
+        if (a.pairing) {
+            auto code_row = [&](int rbx) {
+                const int bh = a.blk_heads == 1 ? 0 : hg;
+                return CodeRow<SPT>{a.blk + (((int64_t)b * a.blk_heads + bh) * a.row_blocks + rbx) * a.blk_stride,
+                                    a.blk_stride, a.kv_tiles, n_stages};
+            };
+            const int npairs = a.row_blocks >> 1;
+            if (idx < 2 * npairs) {
+                t.pair = idx >> 1;
+                const int side = idx & 1;
+                const int rb_lo = t.pair, rb_hi = a.row_blocks - 1 - t.pair;
+                const int w_hi = code_row(rb_hi).count(lane);
+                const int w_lo = code_row(rb_lo).count(lane);
+                const int cut = min((w_hi + w_lo + 1) >> 1, w_hi);
+                const bool shared = cut > 0 && cut < w_hi;
+                const int s_cut = shared ? code_row(rb_hi).stage_after(cut, lane) : n_stages;
+                t.beg0 = 0;
+                t.end0 = n_stages;
+                if (side == 0) {
+                    t.rb0 = rb_hi;
+                    t.end0 = s_cut;
+                    t.side0 = shared ? 0 : -1;
+                } else if (shared) {
+                    t.rb0 = rb_hi;
+                    t.beg0 = s_cut;
+                    t.side0 = 1;
+                    t.rb1 = rb_lo;
+                    t.end1 = n_stages;
+                    t.ntask = 2;
+                } else {
+                    t.rb0 = rb_lo;
+                }
+            } else {
+                t.rb0 = npairs;  // the middle row block of an odd count
+            }
+        }
+    }
+    return t;
+}
+
 // Raw buffer descriptors (word 3 of the resource) and the cache policy that makes a
 // buffer access coherent at agent scope (sc1).
 constexpr int kRawBufferFlags = 0x00020000;
