@@ -401,13 +401,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
             // publishes its partial and raises the ready flag, the second waits for the
             // flag (bounded) and merges
             int *arrival = reinterpret_cast<int *>(m_lds + NW * MI * 64);
-            const int slots = a.rows_per_wg * a.heads_per_wg;
             const int64_t pu = ((int64_t)b * a.head_groups + hg) * (a.row_blocks >> 1) + pair;
             constexpr int PBYTES = DBLK * 64 * 16;  // one wave's partial
-            if (threadIdx.x == 0)
-                *arrival = (int)__hip_atomic_fetch_add(a.pair_cnt + 2 * pu, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __syncthreads();
-            write_final = *arrival != 0;
+            write_final = pair_arrive(a, pu, arrival);
             if (!write_final) {
                 const __amdgpu_buffer_rsrc_t mine = __builtin_amdgcn_make_buffer_rsrc(
                     a.pair_part + ((pu * 2 + side) * NW + wave) * (PBYTES / 4), 0, PBYTES, kRawBufferFlags);
@@ -415,43 +411,15 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(NW / 4,
                 for (int db = 0; db < DBLK; ++db)
                     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(uint4v, acc_o[db]), mine,
                                                            (db * 64 + lane) * 16, 0, kAgentCoherent);
-                if (g4 == 0) {
-                    __hip_atomic_store(&a.pair_ml[(pu * 2 + side) * slots + slot].x, m_run, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(&a.pair_ml[(pu * 2 + side) * slots + slot].y, l_run, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                }
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial is out
-                __syncthreads();
-                if (threadIdx.x == 0)
-                    __hip_atomic_store(a.pair_cnt + 2 * pu + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (g4 == 0) pair_store_ml(a, pu, side, slot, m_run, l_run);
+                pair_ready(a, pu);
             } else {
-                if (threadIdx.x == 0) {
-                    bool seen = false;
-                    for (int spin = 0; spin < kPairWaitPolls; ++spin) {
-                        if (__hip_atomic_load(a.pair_cnt + 2 * pu + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-                            seen = true;
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(2);
-                    }
-                    if (seen) {
-                        __hip_atomic_fetch_add(a.status + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    } else {
-                        __hip_atomic_fetch_or(a.status, (uint32_t)ATTN_PREFILL_WAIT_EXPIRED, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-                    }
-                    *arrival = seen ? 1 : 2;
-                }
-                __syncthreads();
-                gave_up = *arrival == 2;
+                gave_up = pair_wait(a, pu, arrival);
             }
             if (write_final && !gave_up) {
                 const int other = 1 - side;
-                const float mo = __hip_atomic_load(&a.pair_ml[(pu * 2 + other) * slots + slot].x, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-                const float lo = __hip_atomic_load(&a.pair_ml[(pu * 2 + other) * slots + slot].y, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
+                const float2 mlo = pair_load_ml(a, pu, other, slot);
+                const float mo = mlo.x, lo = mlo.y;
                 const float mx = fmaxf(m_run, mo);
                 const float wa = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - mx);
                 const float wb = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - mx);

@@ -265,6 +265,68 @@ __device__ __forceinline__ PrefillTasks prefill_tasks(const PrefillArgs &a, int 
     return t;
 }
 
+// The cut-pair protocol of the two workgroups that share a cut row block (pair unit pu):
+// counters pair_cnt[2 pu] (arrivals) and pair_cnt[2 pu + 1] (partial ready), both zeroed
+// by the classify pass.  The first side to arrive publishes its unnormalised partial O
+// and (m, l) and raises the ready flag; the second side waits for the flag (bounded) and
+// merges.  The two sides may run on different XCDs, whose L2 caches are not coherent with
+// each other: the partials are written and read with agent-coherent (sc1) accesses and
+// only the ready flag orders them, so no fence has to write back or invalidate an L2.
+// `flag` is an LDS word every thread of the workgroup can read.
+
+// True when this workgroup arrives second (it merges), false when first (it publishes).
+__device__ __forceinline__ bool pair_arrive(const PrefillArgs &a, int64_t pu, int *flag) {
+    if (threadIdx.x == 0)
+        *flag = (int)__hip_atomic_fetch_add(a.pair_cnt + 2 * pu, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    return *flag != 0;
+}
+// The publishing side's (m, l) of one query slot.
+__device__ __forceinline__ void pair_store_ml(const PrefillArgs &a, int64_t pu, int side, int slot, float m, float l) {
+    const int slots = a.rows_per_wg * a.heads_per_wg;
+    __hip_atomic_store(&a.pair_ml[(pu * 2 + side) * slots + slot].x, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&a.pair_ml[(pu * 2 + side) * slots + slot].y, l, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// After every wave's partial stores: once they have all completed, raise the ready flag.
+__device__ __forceinline__ void pair_ready(const PrefillArgs &a, int64_t pu) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's partial is out
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(a.pair_cnt + 2 * pu + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// The merging side waits for the ready flag, at most kPairWaitPolls polls, so that no wave
+// can wait forever.  Returns true when it gave up: the partner's partial is then not used,
+// the row block is written as NaN and the status block records the expiry.  A completed
+// wait counts one merged row block in the status block.
+__device__ __forceinline__ bool pair_wait(const PrefillArgs &a, int64_t pu, int *flag) {
+    if (threadIdx.x == 0) {
+        bool seen = false;
+        for (int spin = 0; spin < kPairWaitPolls; ++spin) {
+            if (__hip_atomic_load(a.pair_cnt + 2 * pu + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+                seen = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(2);
+        }
+        if (seen) {
+            __hip_atomic_fetch_add(a.status + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+            __hip_atomic_fetch_or(a.status, (uint32_t)ATTN_PREFILL_WAIT_EXPIRED, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+        }
+        *flag = seen ? 1 : 2;
+    }
+    __syncthreads();
+    return *flag == 2;
+}
+// The other side's (m, l) of one query slot (complete before its ready flag, which the
+// caller has observed).
+__device__ __forceinline__ float2 pair_load_ml(const PrefillArgs &a, int64_t pu, int other, int slot) {
+    const int slots = a.rows_per_wg * a.heads_per_wg;
+    return make_float2(
+        __hip_atomic_load(&a.pair_ml[(pu * 2 + other) * slots + slot].x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+        __hip_atomic_load(&a.pair_ml[(pu * 2 + other) * slots + slot].y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
 // Raw buffer descriptors (word 3 of the resource) and the cache policy that makes a
 // buffer access coherent at agent scope (sc1).
 constexpr int kRawBufferFlags = 0x00020000;
