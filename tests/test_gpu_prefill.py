@@ -147,6 +147,26 @@ def test_fully_masked_rows_are_zero(orc):
     assert_close(got, _oracle(orc, case), "masked rows")
 
 
+@pytest.mark.parametrize("d", [128, 256, 512])
+@pytest.mark.parametrize("kv_dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("rows,kv_len,masked", [(1, 1, False), (1, 65, True), (5, 1, False), (3, 33, True)])
+def test_smallest_shapes(orc, d, kv_dtype, rows, kv_len, masked):
+    """One query row, one key, and other shapes smaller than a single tile: the ragged
+    stage is the only stage, and (with one key) every row's softmax is a single 1."""
+    announce("prefill small shape rows=%d kv=%d d=%d %s masked=%s" % (rows, kv_len, d, kv_dtype, masked))
+    case = workloads.prefill_synthetic("t", rows=rows, kv_len=kv_len, cached=kv_len - rows if kv_len >= rows else 0,
+                                       n_heads=4, n_kv_heads=2, head_dim=d, seed=26, q_std=1 / math.sqrt(d),
+                                       kv_std=1.0, kv_dtype=kv_dtype)
+    got = _run(case, mask=masked)
+    assert_close(got, _oracle(orc, case, mask=masked), "small shape")
+    if kv_len == 1 and not masked:
+        # softmax over one key is 1: O is that key's V (as the kernel's K/V type holds it)
+        v0 = case.v[:, 0].astype(np.float64) if case.v.dtype != np.uint16 else None
+        if v0 is not None:
+            want = np.repeat(v0, 2, axis=1)[:, None]  # [B, 1, H, D] from [B, HK, D], 2 query heads per KV head
+            assert np.array_equal(got, np.broadcast_to(want, got.shape).astype(np.float32))
+
+
 def test_padded_and_unpadded_kv_agree(orc):
     announce("prefill padded vs unpadded KV")
     case = workloads.prefill_synthetic("t", rows=64, kv_len=190, cached=126, n_heads=4, n_kv_heads=1, head_dim=512,
