@@ -102,6 +102,8 @@ def attention(q, k, v, mask=None, *, scale: float, q_bf16=False, kv_bf16=False, 
     if mask is not None and mask.strides[-1] != mask.itemsize:
         mask = np.ascontiguousarray(mask)
     o = np.zeros((B, R, H, D), dtype=np.float64)
+    if KV == 0:
+        return o  # no keys: every row sees nothing and is 0, as for a fully masked row
     qs, ks, vs = _strides(q), _strides(k), _strides(v)
     if mask is not None:
         assert mask.shape[0] == B and mask.shape[2] == R and mask.shape[3] == KV

@@ -100,6 +100,23 @@ def test_fully_masked_row_is_zero(orc):
     assert np.any(o[0, 0] != 0.0)
 
 
+def test_no_keys_equals_every_key_masked(orc):
+    """With no keys at all a row sees nothing, as with every key masked: O = 0.  The
+    paged form at cap 0 gives such rows for the new tokens and NaN past them."""
+    q = _rand((1, 3, 2, 8), 9)
+    empty = orc.attention(q, np.zeros((1, 0, 1, 8)), np.zeros((1, 0, 1, 8)), None, scale=1.0)
+    k, v = _rand((1, 2, 1, 8), 10), _rand((1, 2, 1, 8), 11)
+    masked = orc.attention(q, k, v, np.full((1, 1, 3, 2), -np.inf), scale=1.0)
+    assert empty.shape == masked.shape and np.all(empty == 0.0) and np.all(masked == 0.0)
+    mc = workloads.paged_multi_case(max_tokens=4, batch=2, ctx_lo=4, ctx_hi=30, num_pages=8, n_heads=2, n_kv_heads=1,
+                                    head_dim=128, seed=64, query_lens=[3, 1])
+    pc = mc.paged
+    got = orc.paged_prefill(mc.q, pc.k_pool, pc.v_pool, pc.page_table, mc.query_lens, mc.position_starts,
+                            scale=pc.scale, cap=0)
+    assert np.all(got[0, :3] == 0.0) and np.all(np.isnan(got[0, 3:]))
+    assert np.all(got[1, :1] == 0.0) and np.all(np.isnan(got[1, 1:]))
+
+
 def test_no_mask_equals_zero_mask(orc):
     q, k, v = _rand((2, 3, 4, 8), 9), _rand((2, 6, 2, 8), 10), _rand((2, 6, 2, 8), 11)
     a = orc.attention(q, k, v, None, scale=0.3)
