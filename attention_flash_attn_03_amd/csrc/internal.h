@@ -74,6 +74,7 @@ struct MultiPlan {
     int64_t grid;
     size_t ml_offset, ml_bytes;        // (m, l) [batch][max_tokens][n_heads][max_splits] float2
     size_t part_offset, part_bytes;    // O partials [batch][max_tokens][n_heads][max_splits][head_dim] f32
+    size_t npiece_offset, npiece_bytes;  // pieces per unit [batch][hgroups] i32
     size_t workspace_bytes;
 };
 

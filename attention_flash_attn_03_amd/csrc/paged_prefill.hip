@@ -30,6 +30,10 @@ namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kTK = 32;  // keys per tile
+// What starting a piece costs (page ids, the first tiles' round trip, the epilogue), in
+// tiles of the main loop: every unit occupies this many extra places on the line, so a
+// workgroup whose range holds a unit's start gets that many fewer tiles.
+constexpr int kPieceCostTiles = 8;
 constexpr int kPgCap = kMultiMaxTilesPerWorkgroup * kTK + 2;  // page ids of one piece, any page size
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -39,8 +43,9 @@ struct MultiArgs {
     const uint16_t *k_pool, *v_pool;
     const int32_t *page_table, *query_lens, *position_starts;
     float *o;
-    float *part;  // [batch][max_tokens][n_heads][max_splits][D]
-    float2 *ml;   // [batch][max_tokens][n_heads][max_splits]
+    float *part;     // [batch][max_tokens][n_heads][max_splits][D]
+    float2 *ml;      // [batch][max_tokens][n_heads][max_splits]
+    int32_t *npiece; // [batch][hgroups]: pieces of the unit (written by its first piece)
     int64_t q_bs, q_ts, q_hs, o_bs, o_ts, o_hs, page_stride, token_stride, head_stride;
     int batch, n_heads, group, heads_per_wg, qgroups, hgroups, max_tokens, ncols;
     int page_size, page_shift, max_pages, num_pages, ctx_cap;
@@ -64,6 +69,9 @@ __device__ __forceinline__ SeqInfo seq_info(const MultiArgs &a, int b) {
     return s;
 }
 
+// Places of one unit of `tiles` tiles on the line: its start-up cost, then its tiles.
+__device__ __forceinline__ int unit_span(int tiles) { return tiles > 0 ? kPieceCostTiles + tiles : 0; }
+
 __device__ __forceinline__ int64_t scan_lanes(int64_t x, int lane) {
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -73,19 +81,19 @@ __device__ __forceinline__ int64_t scan_lanes(int64_t x, int lane) {
     return x;
 }
 
-// The sequence whose units hold line tile `pos`, searching from sequence b0 whose
+// The sequence whose units hold line place `pos`, searching from sequence b0 whose
 // units start at `base` (wave-wide, 64 sequences per step); false past the end.
 __device__ bool locate_tile(const MultiArgs &a, int64_t pos, int b0, int64_t base, int &b_out, int64_t &start_out) {
     const int lane = threadIdx.x & 63;
     for (; b0 < a.batch; b0 += 64) {
         const int bb = b0 + lane;
-        const int t = bb < a.batch ? seq_info(a, bb).tiles : 0;
-        const int64_t incl = scan_lanes((int64_t)t * a.hgroups, lane);
+        const int sp = bb < a.batch ? unit_span(seq_info(a, bb).tiles) : 0;
+        const int64_t incl = scan_lanes((int64_t)sp * a.hgroups, lane);
         const int64_t total = __shfl(incl, 63);
         if (pos < base + total) {
             const int l = __builtin_ctzll(__ballot(base + incl > pos));
             b_out = b0 + l;
-            start_out = base + __shfl(incl, l) - (int64_t)__shfl(t, l) * a.hgroups;
+            start_out = base + __shfl(incl, l) - (int64_t)__shfl(sp, l) * a.hgroups;
             return true;
         }
         base += total;
@@ -93,7 +101,7 @@ __device__ bool locate_tile(const MultiArgs &a, int64_t pos, int b0, int64_t bas
     return false;
 }
 
-// Tiles per workgroup for a line of `total` tiles: spread over `target` workgroups
+// Places per workgroup for a line of `total` places: spread over `target` workgroups
 // (one round on the chip), within [kMultiMinTilesPerWorkgroup, kMultiMaxTilesPerWorkgroup].
 __device__ __forceinline__ int per_for_line(const MultiArgs &a, int64_t total) {
     int64_t per = (total + a.target - 1) / a.target;
@@ -101,28 +109,34 @@ __device__ __forceinline__ int per_for_line(const MultiArgs &a, int64_t total) {
     return (int)(per > kMultiMaxTilesPerWorkgroup ? kMultiMaxTilesPerWorkgroup : per);
 }
 
-// Tiles per workgroup of this call's line (wave-wide).
-__device__ int tiles_per_workgroup(const MultiArgs &a) {
+// Places per workgroup of this call's line and the sequence whose units hold this
+// workgroup's first place (sb: the line place of its first unit); false when the
+// workgroup is past the line's end (wave-wide).  One pass over the sequences: the first
+// 64 stay in registers for the search.
+__device__ bool workgroup_range(const MultiArgs &a, int &per, int &b, int64_t &sb) {
     const int lane = threadIdx.x & 63;
-    int64_t total = 0;
+    int64_t total = 0, incl0 = 0;
+    int sp0 = 0;
     for (int b0 = 0; b0 < a.batch; b0 += 64) {
         const int bb = b0 + lane;
-        const int64_t t = bb < a.batch ? (int64_t)seq_info(a, bb).tiles * a.hgroups : 0;
-        total += __shfl(scan_lanes(t, lane), 63);
+        const int sp = bb < a.batch ? unit_span(seq_info(a, bb).tiles) : 0;
+        const int64_t incl = scan_lanes((int64_t)sp * a.hgroups, lane);
+        if (b0 == 0) {
+            sp0 = sp;
+            incl0 = incl;
+        }
+        total += __shfl(incl, 63);
     }
-    return per_for_line(a, total);
-}
-
-// Line position of sequence b's first unit (wave-wide).
-__device__ int64_t seq_start(const MultiArgs &a, int b) {
-    const int lane = threadIdx.x & 63;
-    int64_t base = 0;
-    for (int b0 = 0; b0 < b; b0 += 64) {
-        const int bb = b0 + lane;
-        const int64_t t = bb < b ? (int64_t)seq_info(a, bb).tiles * a.hgroups : 0;
-        base += __shfl(scan_lanes(t, lane), 63);
+    per = per_for_line(a, total);
+    const int64_t r0 = (int64_t)blockIdx.x * per;
+    const int64_t first = __shfl(incl0, 63);
+    if (r0 < first) {
+        const int l = __builtin_ctzll(__ballot(incl0 > r0));
+        b = l;
+        sb = __shfl(incl0, l) - (int64_t)__shfl(sp0, l) * a.hgroups;
+        return true;
     }
-    return base;
+    return locate_tile(a, r0, 64, first, b, sb);
 }
 
 __device__ __forceinline__ int page_of(const MultiArgs &a, int t) {
@@ -316,71 +330,118 @@ __global__ __launch_bounds__(64 * NWV * MultiTiling<D>::TEAMS) void multi_partia
     __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[NSTAGE * 2 * TILE];  // [stage][K, V]
     __shared__ int s_pg[kPgCap];
 
-    // line tiles [r0, r1) of this workgroup, cut at unit boundaries into pieces
-    const int per = tiles_per_workgroup(a);
-    const int64_t r0 = (int64_t)blockIdx.x * per, r1 = r0 + per;
-    int b;
+    // line places [r0, r1) of this workgroup, cut at unit boundaries into pieces; a unit
+    // is its start-up places, then its tiles [rs, u1)
+    int per, b;
     int64_t sb;
-    if (!locate_tile(a, r0, 0, 0, b, sb)) return;
+    if (!workgroup_range(a, per, b, sb)) return;
+    const int64_t r0 = (int64_t)blockIdx.x * per, r1 = r0 + per;
     SeqInfo si = seq_info(a, b);
+    int span = unit_span(si.tiles);
     int64_t pos = r0;
     for (;;) {
-        const int hg = (int)((pos - sb) / si.tiles);
-        const int64_t u0 = sb + (int64_t)hg * si.tiles, u1 = u0 + si.tiles;
+        const int hg = (int)((pos - sb) / span);
+        const int64_t u0 = sb + (int64_t)hg * span, rs = u0 + kPieceCostTiles, u1 = u0 + span;
         const int64_t e = u1 < r1 ? u1 : r1;
-        multi_piece<D, NWV, BF16>(a, kv_lds, s_pg, b, si, hg, (int)(pos - u0), (int)(e - u0),
-                                  blockIdx.x - (int)(u0 / per));
+        const int64_t ps = pos > rs ? pos : rs;
+        if (ps < e) {
+            const int split = blockIdx.x - (int)(rs / per);
+            if (split == 0 && threadIdx.x == 0)
+                a.npiece[(int64_t)b * a.hgroups + hg] = (int)((u1 - 1) / per - rs / per + 1);
+            multi_piece<D, NWV, BF16>(a, kv_lds, s_pg, b, si, hg, (int)(ps - rs), (int)(e - rs), split);
+        }
         pos = e;
         if (pos >= r1) break;
-        const int64_t seq_end = sb + (int64_t)si.tiles * a.hgroups;
+        const int64_t seq_end = sb + (int64_t)span * a.hgroups;
         if (pos >= seq_end) {
             if (!locate_tile(a, pos, b + 1, seq_end, b, sb)) break;
             si = seq_info(a, b);
+            span = unit_span(si.tiles);
         }
     }
 }
 
-// One wave per (sequence, token, query head): O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s
-// over the pieces of its unit; rows past the sequence's query length are not written.
-// One pass over the sequences gives both the line length (hence the tiles per
-// workgroup) and the sequence's place on the line.
+// Half a wave per (sequence, token, query head) row: O = sum_s 2^(m_s - M) O_s / sum_s
+// 2^(m_s - M) l_s over the pieces of its unit; rows past the sequence's query length are
+// not written.  Every load the merge needs (the sequence's lengths, the unit's piece
+// count, the first 32 (m, l) and the first NP slices) is issued at once, whatever the
+// count turns out to be, so a row of at most NP pieces costs one memory round trip;
+// slots past the count are never used (they may hold anything).
 template <int D>
 __global__ __launch_bounds__(256) void multi_merge_kernel(MultiArgs a) {
-    constexpr int PER_LANE = D / 64;
-    const int lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, token, head)
-    if (row >= (int64_t)a.batch * a.max_tokens * a.n_heads) return;
+    constexpr int PER = D / 32;  // floats per lane
+    constexpr int NV = PER / 4;  // float4 per lane and piece
+    constexpr int NP = 4;        // pieces loaded up front
+    const int lane = threadIdx.x & 63, l32 = lane & 31, hbase = lane & 32;
+    const int64_t rows = (int64_t)a.batch * a.max_tokens * a.n_heads;
+    const int64_t wrow = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * 2;
+    if (wrow >= rows) return;  // the whole wave
+    const bool valid = wrow + (lane >> 5) < rows;
+    const int64_t row = valid ? wrow + (lane >> 5) : rows - 1;
     const int head = (int)(row % a.n_heads);
     const int qi = (int)((row / a.n_heads) % a.max_tokens);
     const int b = (int)(row / ((int64_t)a.n_heads * a.max_tokens));
-    // one pass over the sequences' lengths gives this row's sequence (from its lane of the
-    // pass) and the start of its units on the line: one memory round trip before the merge
-    int64_t total = 0, start = 0;
-    int tokens = 0, tiles = 0;
-    for (int b0 = 0; b0 < a.batch; b0 += 64) {
-        const int bb = b0 + lane;
-        const SeqInfo sb = bb < a.batch ? seq_info(a, bb) : SeqInfo{0, 0, 0, 0};
-        const int64_t t = (int64_t)sb.tiles * a.hgroups;
-        const int64_t incl = scan_lanes(t, lane);
-        if (b >= b0 && b < b0 + 64) {
-            start = total + __shfl(incl - t, b - b0);
-            tokens = __shfl(sb.tokens, b - b0);
-            tiles = __shfl(sb.tiles, b - b0);
-        }
-        total += __shfl(incl, 63);
-    }
-    if (qi >= tokens) return;
-    const int per = per_for_line(a, total);
     const int hg = (head / a.group) * a.qgroups + (head % a.group) / a.heads_per_wg;
-    const int64_t u0 = start + (int64_t)hg * tiles;
-    int nsplit = tiles == 0 ? 0 : (int)((u0 + tiles - 1) / per - u0 / per + 1);
-    if (nsplit > a.max_splits) nsplit = a.max_splits;
-    float o[PER_LANE], lsum;
-    merge_pieces<D>(a.ml + row * a.max_splits, a.part + row * a.max_splits * D, nsplit, lane, o, lsum);
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    float *orow = a.o + b * a.o_bs + (int64_t)qi * a.o_ts + (int64_t)head * a.o_hs + lane * PER_LANE;
+
+    const SeqInfo si = seq_info(a, b);
+    const int np_raw = a.npiece[(int64_t)b * a.hgroups + hg];
+    const float2 *mlr = a.ml + row * a.max_splits;
+    const float *pr = a.part + row * a.max_splits * D + l32 * PER;
+    const float2 my0 = l32 < a.max_splits ? mlr[l32] : make_float2(-INFINITY, 0.f);
+    float4v v0[NP][NV];
 #pragma unroll
-    for (int i = 0; i < PER_LANE; ++i) orow[i] = o[i] * inv;
+    for (int u = 0; u < NP; ++u)
+#pragma unroll
+        for (int i = 0; i < NV; ++i)
+            v0[u][i] = u < a.max_splits ? *reinterpret_cast<const float4v *>(pr + (int64_t)u * D + 4 * i)
+                                        : float4v{0.f, 0.f, 0.f, 0.f};
+    // a unit without tiles (no visible key) has no pieces and a row of zeros
+    const int nsplit = si.tiles == 0 ? 0 : min(max(np_raw, 0), a.max_splits);
+
+    float mmax = l32 < nsplit ? my0.x : -INFINITY;
+    for (int s = 32 + l32; s < nsplit; s += 32) mmax = fmaxf(mmax, mlr[s].x);
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, off));
+    float4v o[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) o[i] = float4v{0.f, 0.f, 0.f, 0.f};
+    float lsum = 0.f;
+    if (mmax != -INFINITY) {
+        for (int s0 = 0; s0 < nsplit; s0 += 32) {
+            const bool mine = s0 + l32 < nsplit;
+            const float2 m2 = s0 == 0 ? my0 : (mine ? mlr[s0 + l32] : make_float2(-INFINITY, 0.f));
+            const float w = mine && m2.x != -INFINITY ? exp2f(m2.x - mmax) : 0.f;
+            float lw = w > 0.f ? w * m2.y : 0.f;
+#pragma unroll
+            for (int off = 16; off >= 1; off >>= 1) lw += __shfl_xor(lw, off);
+            lsum += lw;
+            const int n = min(32, nsplit - s0);
+            for (int j = 0; j < n; j += NP) {
+                if (s0 > 0 || j > 0) {  // past the slices loaded up front: load the next NP into v0
+#pragma unroll
+                    for (int u = 0; u < NP; ++u)
+#pragma unroll
+                        for (int i = 0; i < NV; ++i)
+                            v0[u][i] = j + u < n ? *reinterpret_cast<const float4v *>(
+                                                       pr + (int64_t)(s0 + j + u) * D + 4 * i)
+                                                 : float4v{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+                for (int u = 0; u < NP; ++u) {
+                    const float wj = __shfl(w, hbase | ((j + u) & 31));
+                    if (j + u < n) {
+#pragma unroll
+                        for (int i = 0; i < NV; ++i) o[i] += wj * v0[u][i];
+                    }
+                }
+            }
+        }
+    }
+    if (!valid || qi >= si.tokens) return;
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    float *orow = a.o + b * a.o_bs + (int64_t)qi * a.o_ts + (int64_t)head * a.o_hs + l32 * PER;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) *reinterpret_cast<float4v *>(orow + 4 * i) = o[i] * inv;
 }
 
 template <int D, int NWV, bool BF16>
@@ -390,7 +451,7 @@ hipError_t launch_typed(const MultiArgs &a, int64_t grid, hipStream_t stream) {
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int64_t rows = (int64_t)a.batch * a.max_tokens * a.n_heads;
-    hipLaunchKernelGGL((multi_merge_kernel<D>), dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((multi_merge_kernel<D>), dim3((unsigned)((rows + 7) / 8)), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -430,8 +491,8 @@ int plan_paged_prefill(const attn_paged_prefill_params *p, MultiPlan *plan) {
     // a unit of T tiles overlaps at most ceil(T / per) + 1 workgroup ranges
     plan->max_splits = (int)((tiles_max + kMultiMinTilesPerWorkgroup - 1) / kMultiMinTilesPerWorkgroup + 1);
     plan->target = multi_target_workgroups();
-    // enough workgroups for the longest line at the most tiles per workgroup
-    const int64_t line = (int64_t)p->batch * plan->hgroups * tiles_max;
+    // enough workgroups for the longest line at the most places per workgroup
+    const int64_t line = (int64_t)p->batch * plan->hgroups * (tiles_max + kPieceCostTiles);
     const int64_t need = (line + kMultiMaxTilesPerWorkgroup - 1) / kMultiMaxTilesPerWorkgroup;
     plan->grid = need > plan->target ? need : plan->target;
     const size_t rows = (size_t)p->batch * p->max_tokens * p->n_heads;
@@ -439,7 +500,9 @@ int plan_paged_prefill(const attn_paged_prefill_params *p, MultiPlan *plan) {
     plan->ml_bytes = rows * plan->max_splits * sizeof(float2);
     plan->part_offset = (plan->ml_bytes + 255) & ~(size_t)255;
     plan->part_bytes = rows * plan->max_splits * p->head_dim * sizeof(float);
-    plan->workspace_bytes = plan->part_offset + plan->part_bytes;
+    plan->npiece_offset = (plan->part_offset + plan->part_bytes + 255) & ~(size_t)255;
+    plan->npiece_bytes = (size_t)p->batch * plan->hgroups * sizeof(int32_t);
+    plan->workspace_bytes = plan->npiece_offset + plan->npiece_bytes;
     return ATTN_OK;
 }
 
@@ -457,6 +520,7 @@ hipError_t launch_paged_prefill(const attn_paged_prefill_params *p, const MultiP
     a.o = o;
     a.ml = (float2 *)((uint8_t *)ws + plan->ml_offset);
     a.part = (float *)((uint8_t *)ws + plan->part_offset);
+    a.npiece = (int32_t *)((uint8_t *)ws + plan->npiece_offset);
     a.q_bs = p->q_bs;
     a.q_ts = p->q_ts;
     a.q_hs = p->q_hs;

@@ -6,8 +6,9 @@ Covers block verify straight from the page table (16 tokens, 32/8 heads),
 chunks of 64 tokens (MHA), a head_dim 256 group of 3, bf16 pools, odd page
 sizes, sequences with no new tokens (their rows untouched), a fresh prefill
 from position 0, NaN in unused pool slots, strided Q/O, one token per
-sequence against attn_paged_decode, and the same logical KV under two
-physical page placements (bit-identical)."""
+sequence against attn_paged_decode, the same logical KV under two
+physical page placements (bit-identical), max_context 0 (zero rows), a
+workspace of arbitrary bytes, and replays of a captured HIP graph."""
 import numpy as np
 import pytest
 import torch
@@ -151,3 +152,97 @@ def test_page_placement_is_invisible(orc):
     b = _run(moved)
     assert np.array_equal(a, b)
     _check(a, _oracle(orc, mc), mc, "paged prefill")
+
+
+def test_no_context_gives_zero_rows(orc):
+    """max_context 0: no query sees a key; the rows of the new tokens are 0 (the oracle's
+    value for a row with no visible key), the rows past each query length untouched."""
+    announce("paged prefill with max_context 0")
+    mc = workloads.paged_multi_case(max_tokens=5, batch=3, ctx_lo=5, ctx_hi=60, num_pages=12, n_heads=4,
+                                    n_kv_heads=2, head_dim=128, seed=81, query_lens=[5, 0, 2])
+    pc = mc.paged
+    out = torch.full(mc.q.shape, SENTINEL, dtype=torch.float32, device="cuda")
+    fa.attn_paged_prefill(dev(mc.q), dev(pc.k_pool), dev(pc.v_pool), dev(pc.page_table), dev(mc.query_lens),
+                          dev(mc.position_starts), out, scale=pc.scale, max_context=0)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref = orc.paged_prefill(mc.q, pc.k_pool, pc.v_pool, pc.page_table, mc.query_lens, mc.position_starts,
+                            scale=pc.scale, cap=0)
+    _check(got, ref, mc, "max_context 0")
+    assert np.all(got[0] == 0) and np.all(got[2, :2] == 0)
+
+
+def _split_case():
+    # contexts long enough that most (sequence, head group) units are cut into several
+    # pieces that the merge combines
+    return workloads.paged_multi_case(max_tokens=16, batch=6, ctx_lo=2000, ctx_hi=6000, num_pages=2400,
+                                      n_heads=16, n_kv_heads=4, head_dim=128, seed=82)
+
+
+def _call(mc, ws, out):
+    pc = mc.paged
+    fa.attn_paged_prefill(dev(mc.q), dev(pc.k_pool), dev(pc.v_pool), dev(pc.page_table), dev(mc.query_lens),
+                          dev(mc.position_starts), out, scale=pc.scale, max_context=pc.max_context, workspace=ws)
+
+
+def test_workspace_contents_do_not_matter(orc):
+    """The workspace needs no initialisation: one of random bytes, of 0xff bytes, and one
+    reused from the previous call all give the same bits."""
+    announce("paged prefill workspace of random bytes, 0xff bytes, reused")
+    mc = _split_case()
+    pc = mc.paged
+    p = fa.paged_prefill_params(dev(mc.q), dev(pc.k_pool), dev(pc.v_pool), dev(pc.page_table),
+                                torch.empty(mc.q.shape, dtype=torch.float32, device="cuda"), scale=pc.scale,
+                                max_context=pc.max_context)
+    n = fa.paged_prefill_workspace_bytes(p)
+    g = torch.Generator(device="cuda").manual_seed(5)
+    ws = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda", generator=g)
+    outs = []
+    for fill in ("random", "reused", "ff", "reused"):
+        if fill == "ff":
+            ws.fill_(255)
+        out = torch.full(mc.q.shape, SENTINEL, dtype=torch.float32, device="cuda")
+        _call(mc, ws, out)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    for o in outs[1:]:
+        assert np.array_equal(o, outs[0])
+    _check(outs[0], _oracle(orc, mc), mc, "random workspace")
+
+
+def test_graph_replays_match_eager(orc):
+    """One call captured in a HIP graph and replayed four times, with an eager call on the
+    same workspace in between: every replay gives the eager call's bits."""
+    announce("paged prefill captured in a graph, four replays")
+    mc = _split_case()
+    pc = mc.paged
+    q, kp, vp, pt = dev(mc.q), dev(pc.k_pool), dev(pc.v_pool), dev(pc.page_table)
+    ql, ps = dev(mc.query_lens), dev(mc.position_starts)
+    out = torch.full(mc.q.shape, SENTINEL, dtype=torch.float32, device="cuda")
+    p = fa.paged_prefill_params(q, kp, vp, pt, out, scale=pc.scale, max_context=pc.max_context)
+    ws = torch.empty(fa.paged_prefill_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    eager = torch.full_like(out, SENTINEL)
+    fa.attn_paged_prefill(q, kp, vp, pt, ql, ps, eager, scale=pc.scale, max_context=pc.max_context, workspace=ws)
+    torch.cuda.synchronize()
+    want = eager.cpu().numpy()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            fa.attn_paged_prefill(q, kp, vp, pt, ql, ps, out, scale=pc.scale, max_context=pc.max_context,
+                                  workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(SENTINEL)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), want), "replay %d" % rep
+        if rep == 1:  # an eager call (a new tag) on the same workspace between replays
+            fa.attn_paged_prefill(q, kp, vp, pt, ql, ps, eager, scale=pc.scale, max_context=pc.max_context,
+                                  workspace=ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(eager.cpu().numpy(), want)
+    _check(want, _oracle(orc, mc), mc, "graph")
