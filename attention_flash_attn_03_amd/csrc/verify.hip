@@ -315,29 +315,31 @@ __global__ __launch_bounds__(64 * NWV * VerifyTiling<D>::TEAMS) void verify_part
 }
 
 // One wave per (lane, query head, row): O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
-// Every load (the (m, l) of all splits, lane s holding split s, and every split's
-// O slice) is issued before the first use, so the merge costs one memory round trip.
+// The (m, l) of every split slot (lane s holding slot s) and the first NP O slices are
+// requested together with the cache lengths that give the split count, so a row of at
+// most NP splits costs one memory round trip; slots past the count are never used.
 template <int D>
 __global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs a) {
     constexpr int TK = VerifyTiling<D>::TK;
     constexpr int PER_LANE = D / 64;
+    constexpr int NP = 8;  // splits whose slices are loaded up front
     static_assert(kVerifyMaxSplits <= 64, "one split per lane");
     const int lane = threadIdx.x & 63;
     const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (unit >= (int64_t)a.lanes * a.q_heads * a.rows) return;
     const int b = (int)(unit / ((int64_t)a.q_heads * a.rows));
-    const int nsplit = pick4(split_all<TK>(a).splits, b);
     const float2 *ml = a.ml + unit * a.max_splits;
     const float *part = a.part + unit * a.max_splits * D + lane * PER_LANE;
+    const float2 my0 = lane < a.max_splits ? ml[lane] : make_float2(-INFINITY, 0.f);
+    float v[NP][PER_LANE];
+#pragma unroll
+    for (int j = 0; j < NP; ++j)
+#pragma unroll
+        for (int i = 0; i < PER_LANE; ++i) v[j][i] = j < a.max_splits ? part[(int64_t)j * D + i] : 0.f;
+    const int nsplit = pick4(split_all<TK>(a).splits, b);
 
-    const float2 my = lane < nsplit ? ml[lane] : make_float2(-INFINITY, 0.f);
     // every split below nsplit wrote its partial (zeros where it saw no key)
-    float v[kVerifyMaxSplits][PER_LANE];
-#pragma unroll
-    for (int j = 0; j < kVerifyMaxSplits; ++j)
-#pragma unroll
-        for (int i = 0; i < PER_LANE; ++i) v[j][i] = j < nsplit ? part[(int64_t)j * D + i] : 0.f;
-
+    const float2 my = lane < nsplit ? my0 : make_float2(-INFINITY, 0.f);
     float mmax = my.x;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) mmax = fmaxf(mmax, __shfl_xor(mmax, off));
@@ -349,10 +351,17 @@ __global__ __launch_bounds__(256) void verify_merge_kernel(VerifyArgs a) {
 #pragma unroll
     for (int i = 0; i < PER_LANE; ++i) o[i] = 0.f;
 #pragma unroll
-    for (int j = 0; j < kVerifyMaxSplits; ++j) {
+    for (int j = 0; j < NP; ++j) {
+        const float wj = __shfl(w, j);
+        if (j < nsplit) {
+#pragma unroll
+            for (int i = 0; i < PER_LANE; ++i) o[i] = fmaf(wj, v[j][i], o[i]);
+        }
+    }
+    for (int j = NP; j < nsplit; ++j) {
         const float wj = __shfl(w, j);
 #pragma unroll
-        for (int i = 0; i < PER_LANE; ++i) o[i] = fmaf(wj, v[j][i], o[i]);
+        for (int i = 0; i < PER_LANE; ++i) o[i] = fmaf(wj, part[(int64_t)j * D + i], o[i]);
     }
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     float *orow = a.o + unit * D + lane * PER_LANE;
