@@ -10,11 +10,13 @@
 // bytes in flight and keeps the arithmetic off the vector ALUs.
 //  * Split-KV on a balanced line: every (sequence, KV head group) unit owns
 //    ceil(context / 32) tiles of 32 tokens; the units are laid end to end and
-//    workgroup g takes tiles [g*per, (g+1)*per) of that line (cutting it at
-//    unit boundaries), so every workgroup streams the same number of K/V bytes
-//    and the busy workgroups are a dense prefix of the grid.  Each K/V row is
-//    read once for all query heads of its KV head; a second kernel merges the
-//    pieces with a log-sum-exp reduction.
+//    range g is tiles [g*per, (g+1)*per) of that line (cut at unit
+//    boundaries), so every range streams the same number of K/V bytes.  The
+//    grid is the workgroups the chip runs at once; per is set on the device so
+//    the ranges fill the fewest whole rounds of that grid, and workgroup w
+//    takes ranges w, w + grid, ...  Each K/V row is read once for all query
+//    heads of its KV head; a second kernel merges the pieces with a
+//    log-sum-exp reduction.
 //  * The (up to 16) query heads of a KV head are the 16 columns of a
 //    v_mfma_f32_16x16x32 tile: S^T = K Q^T and O^T = V^T P^T run on the
 //    matrix cores; P^T goes from the S^T accumulators straight into the
@@ -27,6 +29,8 @@
 //  * The waves' states are merged in LDS at the end of the chunk.
 #include <math.h>
 
+#include <atomic>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -36,9 +40,14 @@ namespace {
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kTok = 32;      // tokens per wave step
 // the (sequence, KV head group) units are laid end to end as 32-token tiles and
-// every workgroup takes this many of them
-constexpr int kDecodeTilesPerWorkgroup = 32;
-constexpr int kPgCap = kDecodeTilesPerWorkgroup * kTok + 2;  // page ids of one piece, any page size
+// every range takes between this many and (page sizes of 4 tokens and more) four times
+// as many of them
+constexpr int kDecodeMinTilesPerRange = 32;
+constexpr int kDecodeMaxTilesPerRange = 128;
+// page ids of one piece: a piece of kDecodeMinTilesPerRange tiles at page size 1, and of
+// up to 32 * page_size tiles at larger page sizes
+constexpr int kPgCap = kDecodeMinTilesPerRange * kTok + 2;
+constexpr int kDecodeFallbackSlots = 512;  // without a device query
 
 struct DecodeArgs {
     const float *q;
@@ -50,7 +59,8 @@ struct DecodeArgs {
     int64_t q_bs, q_hs, o_bs, o_hs, page_stride, token_stride, head_stride;
     int batch, n_heads, group, heads_per_wg, page_size, page_shift, max_pages, num_pages, ctx_cap;
     int hgroups;     // workgroup head groups per sequence
-    int per;         // tiles (of kTok tokens) per workgroup
+    int per_min, per_max;  // tiles (of kTok tokens) per range
+    int slots;       // workgroups the chip runs at once (the grid)
     int max_splits;  // pieces per unit at most
     float score_scale;
 };
@@ -142,16 +152,25 @@ __device__ bool locate_tile(const DecodeArgs &a, int64_t pos, int b0, int64_t ba
     return false;
 }
 
-// Line position of sequence b's first unit (wave-wide).
-__device__ int64_t seq_start(const DecodeArgs &a, int b) {
+// Tiles per range for a line of `total` tiles: the ranges fill the fewest whole rounds of
+// `slots` workgroups at no more than per_max tiles each, and hold at least per_min.
+__device__ __forceinline__ int per_for_line(const DecodeArgs &a, int64_t total) {
+    const int64_t cap = (int64_t)a.slots * a.per_max;
+    const int64_t rounds = total > cap ? (total + cap - 1) / cap : 1;
+    const int64_t per = (total + rounds * a.slots - 1) / (rounds * a.slots);
+    return (int)(per < a.per_min ? a.per_min : per);
+}
+
+// The line's length in tiles (wave-wide).
+__device__ int64_t line_tiles(const DecodeArgs &a) {
     const int lane = threadIdx.x & 63;
-    int64_t base = 0;
-    for (int b0 = 0; b0 < b; b0 += 64) {
+    int64_t total = 0;
+    for (int b0 = 0; b0 < a.batch; b0 += 64) {
         const int bb = b0 + lane;
-        const int64_t t = bb < b ? (int64_t)seq_tiles(a, bb) * a.hgroups : 0;
-        base += __shfl(scan_lanes(t, lane), 63);
+        const int64_t t = bb < a.batch ? (int64_t)seq_tiles(a, bb) * a.hgroups : 0;
+        total += __shfl(scan_lanes(t, lane), 63);
     }
-    return base;
+    return total;
 }
 
 __device__ __forceinline__ int page_of(const DecodeArgs &a, int t) {
@@ -401,23 +420,28 @@ __global__ __launch_bounds__(64 * NWD) void decode_partial_kernel(DecodeArgs a) 
     __shared__ __attribute__((aligned(1024))) uint16_t kv_lds[NWD * 4 * TILE];   // [wave][buffer][K, V]
     __shared__ int s_pg[kPgCap];
 
-    // line tiles [r0, r1) of this workgroup, cut at unit boundaries into pieces
-    const int64_t r0 = (int64_t)blockIdx.x * a.per, r1 = r0 + a.per;
-    SeqLoc loc;
-    if (!locate_tile(a, r0, 0, 0, loc)) return;
-    int64_t pos = r0;
-    for (;;) {
-        const int hg = (int)((pos - loc.start) / loc.tiles);
-        const int64_t u0 = loc.start + (int64_t)hg * loc.tiles, u1 = u0 + loc.tiles;
-        const int64_t e = u1 < r1 ? u1 : r1;
-        const int ctx = clamp_ctx(a.context_lens[loc.b], a.ctx_cap);
-        const int t0 = (int)(pos - u0) * kTok;
-        const int t1 = min((int)(e - u0) * kTok, ctx);
-        decode_piece<D, NWD, BF16>(a, kv_lds, s_pg, loc.b, hg, t0, t1, blockIdx.x - (int)(u0 / a.per));
-        pos = e;
-        if (pos >= r1) break;
-        const int64_t seq_end = loc.start + (int64_t)loc.tiles * a.hgroups;
-        if (pos >= seq_end && !locate_tile(a, pos, loc.b + 1, seq_end, loc)) break;
+    const int64_t total = line_tiles(a);
+    const int per = per_for_line(a, total);
+    // ranges g = blockIdx.x, blockIdx.x + gridDim.x, ...: line tiles [r0, r1), cut at unit
+    // boundaries into pieces
+    for (int64_t g = blockIdx.x; g * per < total; g += gridDim.x) {
+        const int64_t r0 = g * per, r1 = r0 + per;
+        SeqLoc loc;
+        if (!locate_tile(a, r0, 0, 0, loc)) break;
+        int64_t pos = r0;
+        for (;;) {
+            const int hg = (int)((pos - loc.start) / loc.tiles);
+            const int64_t u0 = loc.start + (int64_t)hg * loc.tiles, u1 = u0 + loc.tiles;
+            const int64_t e = u1 < r1 ? u1 : r1;
+            const int ctx = clamp_ctx(a.context_lens[loc.b], a.ctx_cap);
+            const int t0 = (int)(pos - u0) * kTok;
+            const int t1 = min((int)(e - u0) * kTok, ctx);
+            decode_piece<D, NWD, BF16>(a, kv_lds, s_pg, loc.b, hg, t0, t1, (int)(g - u0 / per));
+            pos = e;
+            if (pos >= r1) break;
+            const int64_t seq_end = loc.start + (int64_t)loc.tiles * a.hgroups;
+            if (pos >= seq_end && !locate_tile(a, pos, loc.b + 1, seq_end, loc)) break;
+        }
     }
 }
 
@@ -430,9 +454,24 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
     const int64_t unit = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (unit >= (int64_t)a.batch * a.n_heads) return;
     const int b = unit / a.n_heads, head = unit % a.n_heads;
-    const int tiles = seq_tiles(a, b);
-    const int64_t u0 = seq_start(a, b) + (int64_t)(head / a.heads_per_wg) * tiles;
-    int nsplit = tiles == 0 ? 0 : (int)((u0 + tiles - 1) / a.per - u0 / a.per + 1);
+    // one pass over the lengths: the line's length (hence the tiles per range) and the
+    // start of sequence b's units
+    int64_t total = 0, start = 0;
+    int tiles = 0;
+    for (int b0 = 0; b0 < a.batch; b0 += 64) {
+        const int bb = b0 + lane;
+        const int tb = bb < a.batch ? seq_tiles(a, bb) : 0;
+        const int64_t t = (int64_t)tb * a.hgroups;
+        const int64_t incl = scan_lanes(t, lane);
+        if (b >= b0 && b < b0 + 64) {
+            start = total + __shfl(incl - t, b - b0);
+            tiles = __shfl(tb, b - b0);
+        }
+        total += __shfl(incl, 63);
+    }
+    const int per = per_for_line(a, total);
+    const int64_t u0 = start + (int64_t)(head / a.heads_per_wg) * tiles;
+    int nsplit = tiles == 0 ? 0 : (int)((u0 + tiles - 1) / per - u0 / per + 1);
     if (nsplit > a.max_splits) nsplit = a.max_splits;
     float o[PER_LANE], lsum;
     merge_pieces<D>(a.ml + unit * a.max_splits, a.part + unit * a.max_splits * D, nsplit, lane, o, lsum);
@@ -440,6 +479,28 @@ __global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs a) {
     float *orow = a.o + b * a.o_bs + (int64_t)head * a.o_hs + lane * PER_LANE;
 #pragma unroll
     for (int i = 0; i < PER_LANE; ++i) orow[i] = o[i] * inv;
+}
+
+// Workgroups of decode_partial_kernel<D, 1, BF16> the current device runs at once,
+// looked up once per (device, kernel); CUs x 2 if the runtime cannot say.
+template <int D, bool BF16>
+int decode_slots_typed() {
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> cache[kMaxDevices] = {};
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return kDecodeFallbackSlots;
+    if (dev < kMaxDevices && cache[dev].load() > 0) return cache[dev].load();
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return kDecodeFallbackSlots;
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(
+                                                                   &decode_partial_kernel<D, 1, BF16>),
+                                                     64, 0) != hipSuccess ||
+        per_cu <= 0)
+        per_cu = 2;
+    const int slots = cus * per_cu;
+    if (dev < kMaxDevices) cache[dev].store(slots);
+    return slots;
 }
 
 template <int D, bool BF16>
@@ -453,6 +514,14 @@ hipError_t launch_typed(const DecodeArgs &a, int64_t grid, hipStream_t stream) {
     const int64_t units = (int64_t)a.batch * a.n_heads;
     hipLaunchKernelGGL((decode_reduce_kernel<D>), dim3((unsigned)((units + 3) / 4)), dim3(256), 0, stream, a);
     return hipGetLastError();
+}
+
+int decode_slots(int head_dim, bool bf16) {
+    switch (head_dim) {
+    case 128: return bf16 ? decode_slots_typed<128, true>() : decode_slots_typed<128, false>();
+    case 256: return bf16 ? decode_slots_typed<256, true>() : decode_slots_typed<256, false>();
+    default: return kDecodeFallbackSlots;
+    }
 }
 
 }  // namespace
@@ -470,11 +539,13 @@ int plan_decode(const attn_decode_params *p, DecodePlan *plan) {
     if (table_cap < cap) cap = (int)table_cap;
     if (cap < 0) cap = 0;
     const int64_t tiles_max = ((int64_t)cap + kTok - 1) / kTok;
-    plan->per = kDecodeTilesPerWorkgroup;
-    // a unit of T tiles overlaps at most ceil(T / per) + 1 workgroup ranges
+    plan->per = kDecodeMinTilesPerRange;
+    // a unit of T tiles overlaps at most ceil(T / per) + 1 ranges, per >= the minimum
     plan->max_splits = (int)((tiles_max + plan->per - 1) / plan->per + 1);
-    const int64_t line = (int64_t)p->batch * plan->hgroups * tiles_max;
-    plan->grid = line > 0 ? (line + plan->per - 1) / plan->per : 1;
+    // page ids of a range's piece must fit the kernel's page-id buffer
+    const int64_t fit = (int64_t)(kPgCap - 2) * p->page_size / kTok;
+    plan->per_max = (int)(fit < kDecodeMaxTilesPerRange ? (fit > plan->per ? fit : plan->per) : kDecodeMaxTilesPerRange);
+    plan->grid = decode_slots(p->head_dim, p->kv_dtype == ATTN_BF16);
     const size_t units = (size_t)p->batch * p->n_heads;
     plan->ml_offset = 0;
     plan->ml_bytes = units * plan->max_splits * sizeof(float2);
@@ -515,7 +586,9 @@ hipError_t launch_paged_decode(const attn_decode_params *p, const DecodePlan *pl
     if (table_cap < cap) cap = (int)table_cap;
     a.ctx_cap = cap < 0 ? 0 : cap;
     a.hgroups = plan->hgroups;
-    a.per = plan->per;
+    a.per_min = plan->per;
+    a.per_max = plan->per_max;
+    a.slots = (int)plan->grid;
     a.max_splits = plan->max_splits;
     a.score_scale = p->scale * kLog2e;
     int shift = -1;

@@ -49,9 +49,9 @@ struct DecodePlan {
     int head_dim, group;              // query heads per KV head
     int heads_per_wg;                 // query heads one workgroup serves
     int hgroups;                      // workgroup head groups per sequence
-    int per;                          // tiles per workgroup
+    int per, per_max;                 // tiles per range: at least per, at most per_max
     int max_splits;                   // pieces per unit at most
-    int64_t grid;                     // workgroups
+    int64_t grid;                     // workgroups (the ones the device runs at once)
     size_t part_offset, part_bytes;   // O partials [batch][n_heads][max_splits][D] f32
     size_t ml_offset, ml_bytes;       // (m, l) [batch][n_heads][max_splits] float2
     size_t workspace_bytes;
