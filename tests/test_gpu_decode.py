@@ -3,9 +3,9 @@
 empty contexts, NaN-poisoned unused slots, the interleaved K/V token record,
 paged == contiguous (through attn_prefill, within a bound derived from the f16
 rounding of P), the same logical KV under two different physical page
-placements (bit-identical), and the full-size
-paged-decode configuration (64 sequences, contexts 512..16384, 65536-page
-pool), every sequence, in the benchmark's launch configuration."""
+placements (bit-identical), the full-size paged-decode configuration (64
+sequences, contexts 512..16384, 65536-page pool), every sequence, in the
+benchmark's launch configuration, and replays of a captured HIP graph."""
 import math
 
 import numpy as np
@@ -159,3 +159,43 @@ def test_full_size_config_every_sequence(orc):
     case = workloads.paged_case()
     got = _run(case)
     assert_close(got, _oracle(orc, case), "decode full size")
+
+
+def test_graph_replays_match_eager(orc):
+    """attn_paged_decode captured in a HIP graph (its grid sized from the device's
+    occupancy, its tiles per range set on the device) and replayed four times, with an
+    eager call on the same workspace between replays: every replay gives the eager bits."""
+    announce("paged decode captured in a graph, four replays")
+    case = workloads.paged_case(batch=12, ctx_lo=200, ctx_hi=9000, num_pages=8000, n_heads=32, n_kv_heads=8,
+                                head_dim=128, seed=91)
+    q, kp, vp = dev(case.q), dev(case.k_pool), dev(case.v_pool)
+    pt, ctx = dev(case.page_table), dev(case.context_lens)
+    out = torch.full(case.q.shape, float("nan"), dtype=torch.float32, device="cuda")
+    p = fa.decode_params(q, kp, vp, pt, out, scale=case.scale, max_context=case.max_context)
+    ws = torch.empty(fa.decode_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    eager = torch.full_like(out, float("nan"))
+    fa.attn_paged_decode(q, kp, vp, pt, ctx, eager, scale=case.scale, max_context=case.max_context, workspace=ws)
+    torch.cuda.synchronize()
+    want = eager.cpu().numpy()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            fa.attn_paged_decode(q, kp, vp, pt, ctx, out, scale=case.scale, max_context=case.max_context,
+                                 workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(out.cpu().numpy(), want), "replay %d" % rep
+        if rep == 1:
+            fa.attn_paged_decode(q, kp, vp, pt, ctx, eager, scale=case.scale, max_context=case.max_context,
+                                 workspace=ws)
+            torch.cuda.synchronize()
+            assert np.array_equal(eager.cpu().numpy(), want)
+    ref = orc.paged_decode(case.q, case.k_pool, case.v_pool, case.page_table, case.context_lens, scale=case.scale)
+    assert_close(want, ref, "graph decode")
