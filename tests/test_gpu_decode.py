@@ -1,6 +1,6 @@
 """GPU parity of attn_paged_decode against the fp64 oracle, elementwise within
 |err| <= 2e-3 * (1 + |ref|): oracle-sized page tables, bf16 and head_dim 256,
-empty contexts, NaN-poisoned unused slots, the interleaved K/V token record,
+page sizes 1-3 with contexts of up to 16k tokens, empty contexts, NaN-poisoned unused slots, the interleaved K/V token record,
 paged == contiguous (through attn_prefill, within a bound derived from the f16
 rounding of P), the same logical KV under two different physical page
 placements (bit-identical), the full-size paged-decode configuration (64
@@ -48,6 +48,18 @@ def test_decode_oracle_sized(orc, kw):
     announce("decode %s" % kw)
     case = workloads.paged_case(**kw)
     assert_close(_run(case), _oracle(orc, case), "decode")
+
+
+@pytest.mark.parametrize("page_size", [1, 2, 3])
+def test_small_pages_long_contexts(orc, page_size):
+    """Page sizes below 4 bound the tiles per range by the page-id buffer (32 * page_size
+    tiles); contexts long enough (about 160k tokens over 8 KV heads) that the device sets
+    more than the minimum 32 tiles per range where that bound allows it.  Every row."""
+    announce("decode page_size %d, long contexts" % page_size)
+    case = workloads.paged_case(batch=12, ctx_lo=11000, ctx_hi=16000, page_size=page_size,
+                                num_pages=-(-12 * 16000 // page_size), n_heads=32, n_kv_heads=8, head_dim=128,
+                                seed=36 + page_size)
+    assert_close(_run(case), _oracle(orc, case), "decode small pages")
 
 
 def test_empty_and_one_token_contexts(orc):
