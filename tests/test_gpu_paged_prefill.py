@@ -8,7 +8,8 @@ sizes, sequences with no new tokens (their rows untouched), a fresh prefill
 from position 0, NaN in unused pool slots, strided Q/O, one token per
 sequence against attn_paged_decode, the same logical KV under two
 physical page placements (bit-identical), max_context 0 (zero rows), a
-workspace of arbitrary bytes, and replays of a captured HIP graph."""
+workspace of arbitrary bytes, replays of a captured HIP graph, and the
+benchmark's full-size workload (four sequences checked row by row)."""
 import numpy as np
 import pytest
 import torch
@@ -246,3 +247,20 @@ def test_graph_replays_match_eager(orc):
             torch.cuda.synchronize()
             assert np.array_equal(eager.cpu().numpy(), want)
     _check(want, _oracle(orc, mc), mc, "graph")
+
+
+def test_full_size_multi_token_workload(orc):
+    """The benchmark's multi-token workload (16 sequences x 16 new tokens over contexts of
+    1k-8k tokens, 32/8 heads, d 128, 8192-page pool) in its launch configuration; every
+    row of four sequences spread over the batch against the oracle (units cut into pieces
+    across workgroups among them), the other rows finite."""
+    announce("paged prefill full-size multi-token workload")
+    mc = workloads.paged_multi_case(max_tokens=16, batch=16, ctx_lo=1024, ctx_hi=8192, num_pages=8192,
+                                    n_heads=32, n_kv_heads=8, head_dim=128, seed=6, query_lens=np.full(16, 16))
+    got = _run(mc)
+    assert np.all(np.isfinite(got))
+    seqs = np.array([0, 5, 10, 15])
+    pc = mc.paged
+    ref = orc.paged_prefill(mc.q[seqs], pc.k_pool, pc.v_pool, pc.page_table[seqs], mc.query_lens[seqs],
+                            mc.position_starts[seqs], scale=pc.scale, cap=pc.max_context)
+    assert_close(got[seqs], ref, "full-size multi-token")
