@@ -8,8 +8,9 @@ sizes, sequences with no new tokens (their rows untouched), a fresh prefill
 from position 0, NaN in unused pool slots, strided Q/O, one token per
 sequence against attn_paged_decode, the same logical KV under two
 physical page placements (bit-identical), max_context 0 (zero rows), a
-workspace of arbitrary bytes, replays of a captured HIP graph, and the
-benchmark's full-size workload (four sequences checked row by row)."""
+workspace of arbitrary bytes, replays of a captured HIP graph, the
+benchmark's full-size workload (four sequences checked row by row), and one
+unit cut into about 40 pieces."""
 import numpy as np
 import pytest
 import torch
@@ -264,3 +265,14 @@ def test_full_size_multi_token_workload(orc):
     ref = orc.paged_prefill(mc.q[seqs], pc.k_pool, pc.v_pool, pc.page_table[seqs], mc.query_lens[seqs],
                             mc.position_starts[seqs], scale=pc.scale, cap=pc.max_context)
     assert_close(got[seqs], ref, "full-size multi-token")
+
+
+def test_unit_of_more_than_32_pieces(orc):
+    """One sequence, one head, a 20k-token context: a line of 633 places spread over one
+    workgroup per CU at the minimum 16 tiles each, so its only unit is cut into about 40
+    pieces and the merge folds (m, l) past the first 32 and slices past the first four."""
+    announce("paged prefill, one unit of about 40 pieces")
+    ctx = np.array([20000], np.int32)
+    mc = workloads.paged_multi_case(max_tokens=4, batch=1, num_pages=1300, n_heads=1, n_kv_heads=1, head_dim=128,
+                                    seed=83, context_lens=ctx, ctx_hi=20000, query_lens=[4])
+    _check(_run(mc), _oracle(orc, mc), mc, "many pieces")
