@@ -1,6 +1,7 @@
 """GPU parity of attn_paged_decode against the fp64 oracle, elementwise within
 |err| <= 2e-3 * (1 + |ref|): oracle-sized page tables, bf16 and head_dim 256,
-page sizes 1-3 with contexts of up to 16k tokens, empty contexts, NaN-poisoned unused slots, the interleaved K/V token record,
+page sizes 1-3 with contexts of up to 16k tokens, one unit of about 69 pieces,
+empty contexts, NaN-poisoned unused slots, the interleaved K/V token record,
 paged == contiguous (through attn_prefill, within a bound derived from the f16
 rounding of P), the same logical KV under two different physical page
 placements (bit-identical), the full-size paged-decode configuration (64
@@ -60,6 +61,16 @@ def test_small_pages_long_contexts(orc, page_size):
                                 num_pages=-(-12 * 16000 // page_size), n_heads=32, n_kv_heads=8, head_dim=128,
                                 seed=36 + page_size)
     assert_close(_run(case), _oracle(orc, case), "decode small pages")
+
+
+def test_unit_of_more_than_64_pieces(orc):
+    """One sequence, one head, a 70k-token context: the line is short, so ranges take the
+    minimum 32 tiles and the unit is cut into about 69 pieces, past the 64 (m, l) one pass
+    of the reduce reads."""
+    announce("decode, one unit of about 69 pieces")
+    case = workloads.paged_case(batch=1, num_pages=4400, n_heads=1, n_kv_heads=1, head_dim=128, seed=38,
+                                context_lens=np.array([70000], np.int32), ctx_hi=70000)
+    assert_close(_run(case), _oracle(orc, case), "decode many pieces")
 
 
 def test_empty_and_one_token_contexts(orc):
