@@ -9,8 +9,8 @@ from position 0, NaN in unused pool slots, strided Q/O, one token per
 sequence against attn_paged_decode, the same logical KV under two
 physical page placements (bit-identical), max_context 0 (zero rows), a
 workspace of arbitrary bytes, replays of a captured HIP graph, the
-benchmark's full-size workload (four sequences checked row by row), and one
-unit cut into about 40 pieces."""
+benchmark's full-size workload (four sequences checked row by row), one
+unit cut into about 40 pieces, and out-of-range lengths and starts (clamped)."""
 import numpy as np
 import pytest
 import torch
@@ -276,3 +276,30 @@ def test_unit_of_more_than_32_pieces(orc):
     mc = workloads.paged_multi_case(max_tokens=4, batch=1, num_pages=1300, n_heads=1, n_kv_heads=1, head_dim=128,
                                     seed=83, context_lens=ctx, ctx_hi=20000, query_lens=[4])
     _check(_run(mc), _oracle(orc, mc), mc, "many pieces")
+
+
+def test_out_of_range_lengths_and_starts_are_clamped(orc):
+    """Query lengths below 0 or above max_tokens and starts below 0 or past the table's
+    capacity are clamped as the oracle clamps them (lengths to [0, max_tokens], starts to
+    [0, cap], the context to cap); rows past the clamped length are untouched."""
+    announce("paged prefill with out-of-range lengths and starts")
+    base = workloads.paged_multi_case(max_tokens=6, batch=5, ctx_lo=40, ctx_hi=300, num_pages=120, n_heads=4,
+                                      n_kv_heads=2, head_dim=128, seed=84)
+    # every table entry a real page, so that clamped contexts past a sequence's own tokens
+    # read the same (arbitrary) rows on both sides
+    pt = base.paged.page_table.copy()
+    free = np.argwhere(pt < 0)
+    pt[free[:, 0], free[:, 1]] = (7 * free[:, 0] + 3 * free[:, 1]) % base.paged.k_pool.shape[0]
+    pc = workloads.PagedCase(base.paged.q, base.paged.k_pool, base.paged.v_pool, pt, base.paged.context_lens,
+                             base.paged.scale, base.paged.max_context, base.paged.meta)
+    cap = pc.max_context
+    lens = np.array([-3, 99, 4, 6, 2], np.int32)
+    starts = np.array([5, -7, cap + 1000, cap - 2, 30], np.int32)
+    mc = workloads.PagedMultiCase(pc, base.q, lens, starts)
+    got = _run(mc)
+    ref = _oracle(orc, mc)
+    for b in range(5):
+        n = min(max(int(lens[b]), 0), 6)
+        if n:
+            assert_close(got[b, :n], ref[b, :n], "clamped (sequence %d)" % b)
+        assert np.all(got[b, n:] == SENTINEL), "rows past the clamped length were written (sequence %d)" % b
