@@ -1,7 +1,7 @@
 """GPU parity of attn_paged_decode against the fp64 oracle, elementwise within
 |err| <= 2e-3 * (1 + |ref|): oracle-sized page tables, bf16 and head_dim 256,
 page sizes 1-3 with contexts of up to 16k tokens, one unit of about 69 pieces,
-empty contexts, NaN-poisoned unused slots, the interleaved K/V token record,
+context lengths outside [0, max_context] (clamped), empty contexts, NaN-poisoned unused slots, the interleaved K/V token record,
 paged == contiguous (through attn_prefill, within a bound derived from the f16
 rounding of P), the same logical KV under two different physical page
 placements (bit-identical), the full-size paged-decode configuration (64
@@ -71,6 +71,25 @@ def test_unit_of_more_than_64_pieces(orc):
     case = workloads.paged_case(batch=1, num_pages=4400, n_heads=1, n_kv_heads=1, head_dim=128, seed=38,
                                 context_lens=np.array([70000], np.int32), ctx_hi=70000)
     assert_close(_run(case), _oracle(orc, case), "decode many pieces")
+
+
+def test_out_of_range_contexts_are_clamped(orc):
+    """Context lengths below 0 and past max_context are clamped to [0, max_context] (the
+    oracle is given the clamped lengths); a length clamped to 0 gives a zero row."""
+    announce("decode with out-of-range context lengths")
+    case = workloads.paged_case(batch=4, ctx_lo=20, ctx_hi=400, num_pages=120, n_heads=8, n_kv_heads=2,
+                                head_dim=128, seed=39)
+    cap = 300
+    lens = np.array([-5, 50, cap + 100, 2 ** 31 - 1], np.int32)
+    pt = case.page_table.copy()
+    free = np.argwhere(pt < 0)
+    pt[free[:, 0], free[:, 1]] = (5 * free[:, 0] + 11 * free[:, 1]) % case.k_pool.shape[0]
+    moved = workloads.PagedCase(case.q, case.k_pool, case.v_pool, pt, lens, case.scale, cap, case.meta)
+    got = _run(moved, max_context=cap)
+    assert np.all(got[0] == 0.0)
+    clipped = workloads.PagedCase(case.q, case.k_pool, case.v_pool, pt, np.clip(lens, 0, cap).astype(np.int32),
+                                  case.scale, cap, case.meta)
+    assert_close(got, _oracle(orc, clipped), "decode clamped")
 
 
 def test_empty_and_one_token_contexts(orc):
