@@ -18,7 +18,9 @@
 // staged in LDS so any rotation pairing is one read; the work is a few KB per
 // token, so the kernel is bound by launch and latency, not bandwidth.  The
 // angle s * theta^(-2i/rope_dim) is formed and reduced modulo 2 pi in fp64:
-// in f32 it would be off by about 1e-3 radians at positions of 16k.
+// in f32 it would be off by about 1e-3 radians at positions of 16k.  The
+// frequencies theta^(-2i/rope_dim) depend on i alone: the host computes them
+// once, in fp64, and passes the table with the arguments.
 #include <math.h>
 
 #include "device_common.h"
@@ -26,6 +28,8 @@
 
 namespace attn {
 namespace {
+
+constexpr int kPrepareMaxPairs = 128;  // rope_dim <= head_dim <= 256
 
 struct PrepareArgs {
     const float *q_raw, *k_raw, *v_raw, *q_norm, *k_norm;
@@ -39,10 +43,11 @@ struct PrepareArgs {
     int page_size, max_pages, num_pages, ctx_cap;
     int bf16;
     float eps;
-    double log2_theta;
+    double inv_freq[kPrepareMaxPairs];  // theta^(-2i/rope_dim), i < rope_dim / 2
 };
 
 constexpr double kTwoPi = 6.283185307179586476925286766559;
+constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
 
 template <int D>
 __global__ __launch_bounds__(256) void prepare_kernel(PrepareArgs a) {
@@ -112,8 +117,8 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepareArgs a) {
                     partner = first ? d + half : d - half;
                 }
                 // angle = pos * theta^(-2i/rope_dim), reduced modulo 2 pi in fp64
-                const double ang = (double)pos64 * exp2(-a.log2_theta * (2.0 * i) / (double)a.rope_dim);
-                const double red = ang - kTwoPi * floor(ang / kTwoPi);
+                const double ang = (double)pos64 * a.inv_freq[i];
+                const double red = ang - kTwoPi * floor(ang * kInvTwoPi);
                 float sn, cs;
                 sincosf((float)red, &sn, &cs);
                 const float other = s_x[wave][partner];
@@ -192,7 +197,9 @@ hipError_t launch_paged_prepare(const attn_paged_prepare_params *p, const float 
     a.ctx_cap = cap < 0 ? 0 : cap;
     a.bf16 = p->kv_dtype == ATTN_BF16;
     a.eps = p->epsilon;
-    a.log2_theta = log2((double)p->rope_theta);
+    const double log2_theta = log2((double)p->rope_theta);
+    for (int i = 0; i < kPrepareMaxPairs; ++i)
+        a.inv_freq[i] = i < p->rope_dim / 2 ? exp2(-log2_theta * (2.0 * i) / (double)p->rope_dim) : 0.0;
     const int64_t items = (int64_t)p->batch * p->max_tokens * (p->n_heads + 2 * p->n_kv_heads);
     const dim3 grid((unsigned)((items + 3) / 4));
     switch (p->head_dim) {
