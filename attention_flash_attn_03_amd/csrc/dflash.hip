@@ -131,27 +131,36 @@ __global__ __launch_bounds__(kThreads) void mask_kernel(dflash_params p,
     }
 }
 
+// One thread per committed 8-element chunk.  Its indices come from 32-bit arithmetic when
+// the chunks number fewer than 2^32 (IDX = uint32_t); the commit count, the write position
+// and the new row are requested together (the row exists for every c < max_commit), so the
+// call is one memory round trip before the stores.
+template <typename IDX>
 __global__ __launch_bounds__(kThreads) void commit_kernel(
     dflash_params p, const float *__restrict__ new_k, const float *__restrict__ new_v,
     const uint32_t *__restrict__ commit_counts, const uint32_t *__restrict__ write_positions,
     uint16_t *__restrict__ ring_k, uint16_t *__restrict__ ring_v, uint64_t total) {
-    const uint64_t t = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
-    if (t >= total) return;
+    const uint64_t t64 = (uint64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (t64 >= total) return;
+    const IDX t = (IDX)t64;
     const uint32_t chunks = p.head_dim / 8;
-    const uint32_t dc = t % chunks;
-    uint64_t rest = t / chunks;
-    const uint32_t kh = rest % p.kv_heads;
+    const uint32_t dc = (uint32_t)(t % chunks);
+    IDX rest = t / chunks;
+    const uint32_t kh = (uint32_t)(rest % p.kv_heads);
     rest /= p.kv_heads;
-    const uint32_t c = rest % p.max_commit;
-    const uint64_t b = rest / p.max_commit;
-    uint32_t n = commit_counts[b];
-    if (n > p.max_commit) n = p.max_commit;
-    if (c >= n) return;
-    const uint32_t slot = (write_positions[b] % p.window + c) % p.window;
+    const uint32_t c = (uint32_t)(rest % p.max_commit);
+    const uint64_t b = (uint64_t)(rest / p.max_commit);
+    const uint32_t n_raw = commit_counts[b];
+    const uint32_t wp = write_positions[b];
     const uint64_t src = ((b * p.max_commit + c) * p.kv_heads + kh) * p.head_dim + dc * 8;
+    const uint4v kval = load_f32x8_as_bf16(new_k + src);
+    const uint4v vval = load_f32x8_as_bf16(new_v + src);
+    const uint32_t n = n_raw > p.max_commit ? p.max_commit : n_raw;
+    if (c >= n) return;
+    const uint32_t slot = (uint32_t)(((uint64_t)(wp % p.window) + c) % p.window);
     const uint64_t dst = ((b * p.kv_heads + kh) * p.window + slot) * p.head_dim + dc * 8;
-    *reinterpret_cast<uint4v *>(ring_k + dst) = load_f32x8_as_bf16(new_k + src);
-    *reinterpret_cast<uint4v *>(ring_v + dst) = load_f32x8_as_bf16(new_v + src);
+    *reinterpret_cast<uint4v *>(ring_k + dst) = kval;
+    *reinterpret_cast<uint4v *>(ring_v + dst) = vval;
 }
 
 __global__ __launch_bounds__(kThreads) void mask_rows_kernel(uint32_t rows, uint32_t hidden,
@@ -201,8 +210,13 @@ hipError_t launch_dflash_commit(const dflash_params *p, const float *new_k, cons
                                 const uint32_t *commit_counts, const uint32_t *write_positions,
                                 uint16_t *ring_k, uint16_t *ring_v, hipStream_t stream) {
     const uint64_t total = (uint64_t)p->lanes * p->max_commit * p->kv_heads * (p->head_dim / 8);
-    hipLaunchKernelGGL(commit_kernel, dim3(blocks_for(total)), dim3(kThreads), 0, stream, *p, new_k, new_v,
-                       commit_counts, write_positions, ring_k, ring_v, total);
+    if (total < ((uint64_t)1 << 32)) {
+        hipLaunchKernelGGL(commit_kernel<uint32_t>, dim3(blocks_for(total)), dim3(kThreads), 0, stream, *p, new_k,
+                           new_v, commit_counts, write_positions, ring_k, ring_v, total);
+    } else {
+        hipLaunchKernelGGL(commit_kernel<uint64_t>, dim3(blocks_for(total)), dim3(kThreads), 0, stream, *p, new_k,
+                           new_v, commit_counts, write_positions, ring_k, ring_v, total);
+    }
     return hipGetLastError();
 }
 
