@@ -62,11 +62,12 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(
         kval = load_f32x8_as_bf16(cur_k + src);
         vval = load_f32x8_as_bf16(cur_v + src);
     } else {
-        // then the cache, newest first: j-th newest row is ring slot (wp - 1 - j) mod w
+        // then the cache, newest first: j-th newest row is ring slot (wp - 1 - j) mod w;
+        // the lane's length and write position are requested together
         const uint32_t j = pos - p.rows;
         const uint32_t length = cache_lengths[b];
+        const uint32_t wp = write_positions[b] % p.window;
         if (j < length) {
-            const uint32_t wp = write_positions[b] % p.window;
             const uint32_t slot = (wp + p.window - 1 - j) % p.window;
             const uint64_t src = ((b * p.kv_heads + kh) * p.window + slot) * p.head_dim + dc * 8;
             kval = *reinterpret_cast<const uint4v *>(ring_k + src);
