@@ -255,6 +255,9 @@ int check_prepare(const attn_paged_prepare_params *p) {
                                p->kv_token_stride, p->kv_head_stride};
     for (int64_t st : strides)
         if (st < 0) return fail("attn_paged_prepare: negative stride %s", d);
+    // 16-byte row accesses: every f32 stride a multiple of 4 elements, the pools' of 4 (8 bytes)
+    for (int64_t st : strides)
+        if (st % 4) return fail("attn_paged_prepare: strides must be multiples of 4 elements %s", d);
     int64_t need;
     const struct {
         const char *name;
@@ -464,10 +467,10 @@ int attn_paged_prepare(const attn_paged_prepare_params *p, const float *q_raw, c
     if (!q_raw || !k_raw || !v_raw || !page_table || !query_lens || !position_starts || !q_out || !k_pool || !v_pool)
         return fail("attn_paged_prepare: every buffer must be non-NULL");
     if (p->qk_norm && (!q_norm || !k_norm)) return fail("attn_paged_prepare: qk_norm needs both norm weight buffers");
-    if (!aligned(q_raw, 4) || !aligned(k_raw, 4) || !aligned(v_raw, 4) || !aligned(q_out, 4) || !aligned(k_pool, 2) ||
-        !aligned(v_pool, 2) || !aligned(page_table, 4) || !aligned(query_lens, 4) || !aligned(position_starts, 4) ||
-        (p->qk_norm && (!aligned(q_norm, 4) || !aligned(k_norm, 4))))
-        return fail("attn_paged_prepare: buffers must be aligned to their element size");
+    if (!aligned(q_raw, 16) || !aligned(k_raw, 16) || !aligned(v_raw, 16) || !aligned(q_out, 16) ||
+        !aligned(k_pool, 8) || !aligned(v_pool, 8) || !aligned(page_table, 4) || !aligned(query_lens, 4) ||
+        !aligned(position_starts, 4) || (p->qk_norm && (!aligned(q_norm, 16) || !aligned(k_norm, 16))))
+        return fail("attn_paged_prepare: f32 buffers must be 16-byte aligned, the pools 8-byte, the tables 4-byte");
     return hip_status(attn::launch_paged_prepare(p, q_raw, k_raw, v_raw, q_norm, k_norm, page_table, query_lens,
                                                  position_starts, q_out, k_pool, v_pool, (hipStream_t)stream),
                       "attn_paged_prepare");

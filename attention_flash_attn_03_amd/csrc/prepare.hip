@@ -49,88 +49,108 @@ struct PrepareArgs {
 constexpr double kTwoPi = 6.283185307179586476925286766559;
 constexpr double kInvTwoPi = 0.15915494309189533576888376337251;
 
+// Half a wave (32 lanes) per (sequence, token, head slot) item, two items per wave: lane
+// l of a half holds features 4l + 128k .. 4l + 128k + 3 (k < D / 128), so the row is read
+// and written with 16-byte accesses.  Every load that does not depend on another (the
+// sequence's query length and start, the features, the norm weights) is issued before any
+// is used; only the page entry waits for the start.
 template <int D>
 __global__ __launch_bounds__(256) void prepare_kernel(PrepareArgs a) {
-    constexpr int PER = D / 64;  // features per lane: d = lane + 64*k
-    __shared__ float s_x[4][D];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int NV = D / 128;  // float4 per lane
+    __shared__ float s_x[8][D];  // one row per half wave
+    const int lane = threadIdx.x & 63, l32 = lane & 31;
+    const int half_id = threadIdx.x >> 5;  // 0..7 within the workgroup
     const int slots = a.n_heads + 2 * a.n_kv_heads;
-    const int64_t item = (int64_t)blockIdx.x * 4 + wave;  // (b, t, slot)
-    if (item >= (int64_t)a.batch * a.max_tokens * slots) return;
-    const int slot = (int)(item % slots);
-    const int t = (int)((item / slots) % a.max_tokens);
-    const int b = (int)(item / ((int64_t)slots * a.max_tokens));
+    const int64_t items = (int64_t)a.batch * a.max_tokens * slots;
+    const int64_t item = (int64_t)blockIdx.x * 8 + half_id;  // (b, t, slot)
+    const bool live = item < items;
+    const int64_t it = live ? item : items - 1;
+    const int slot = (int)(it % slots);
+    const int t = (int)((it / slots) % a.max_tokens);
+    const int b = (int)(it / ((int64_t)slots * a.max_tokens));
     const bool is_q = slot < a.n_heads, is_k = !is_q && slot < a.n_heads + a.n_kv_heads;
     const int head = is_q ? slot : (is_k ? slot - a.n_heads : slot - a.n_heads - a.n_kv_heads);
-    // Every load that does not depend on another is issued before any is used (one memory
-    // round trip): the sequence's query length and start, the head's features (row t exists
-    // for every t < max_tokens) and its norm weights.  Only the page entry waits for the start.
     const int n_raw = a.query_lens[b];
     const int st_raw = a.position_starts[b];
     const float *src = is_q ? a.q_raw + b * a.qr_bs + (int64_t)t * a.qr_ts + (int64_t)head * a.qr_hs
                             : (is_k ? a.k_raw + b * a.kr_bs + (int64_t)t * a.kr_ts + (int64_t)head * a.kr_hs
                                     : a.v_raw + b * a.vr_bs + (int64_t)t * a.vr_ts + (int64_t)head * a.vr_hs);
-    float x[PER];
+    float4v x[NV], wn[NV];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) x[k] = src[lane + 64 * k];
-    float wn[PER];
-    if ((is_q || is_k) && a.use_norm) {
+    for (int k = 0; k < NV; ++k) x[k] = *reinterpret_cast<const float4v *>(src + 4 * l32 + 128 * k);
+    const bool normed = (is_q || is_k) && a.use_norm;
+    if (normed) {
         const float *w = is_q ? a.q_norm + (int64_t)head * a.qn_hs : a.k_norm + (int64_t)head * a.kn_hs;
 #pragma unroll
-        for (int k = 0; k < PER; ++k) wn[k] = w[lane + 64 * k];
+        for (int k = 0; k < NV; ++k) wn[k] = *reinterpret_cast<const float4v *>(w + 4 * l32 + 128 * k);
     }
     const int n = n_raw < 0 ? 0 : (n_raw > a.max_tokens ? a.max_tokens : n_raw);
-    if (t >= n) return;
     const int st = st_raw < 0 ? 0 : st_raw;
     const int64_t pos64 = (int64_t)st + t;
-    if (!is_q && pos64 >= a.ctx_cap) return;  // past the pages this sequence may use
+    // this item is written: a live row of a new token, and for K/V within the pages the
+    // sequence may use (every lane of a half wave agrees)
+    const bool act = live && t < n && (is_q || pos64 < a.ctx_cap);
 
     if (is_q || is_k) {
-        if (a.use_norm) {
-            float ss = 0.f;
+        // the RMS sum runs over the 32 lanes of the half wave in every half, so that the
+        // shuffles see their partners; inactive halves compute on their clamped item
+        float ss = 0.f;
 #pragma unroll
-            for (int k = 0; k < PER; ++k) ss = fmaf(x[k], x[k], ss);
+        for (int k = 0; k < NV; ++k)
 #pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+            for (int e = 0; e < 4; ++e) ss = fmaf(x[k][e], x[k][e], ss);
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+        if (normed) {
             const float inv = 1.f / sqrtf(ss / (float)D + a.eps);
 #pragma unroll
-            for (int k = 0; k < PER; ++k) x[k] = x[k] * inv * wn[k];
-        }
-        // rotary embedding: the partner of feature d comes from LDS
+            for (int k = 0; k < NV; ++k)
 #pragma unroll
-        for (int k = 0; k < PER; ++k) s_x[wave][lane + 64 * k] = x[k];
-        __builtin_amdgcn_wave_barrier();  // LDS operations of one wave complete in order
+                for (int e = 0; e < 4; ++e) x[k][e] = x[k][e] * inv * wn[k][e];
+        }
+        // rotary embedding; a split-halves partner comes from the half wave's LDS row
+        if (!a.interleaved) {
+#pragma unroll
+            for (int k = 0; k < NV; ++k) *reinterpret_cast<float4v *>(&s_x[half_id][4 * l32 + 128 * k]) = x[k];
+            __builtin_amdgcn_wave_barrier();  // LDS operations of one wave complete in order
+        }
         const int half = a.rope_dim / 2;
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int d = lane + 64 * k;
-            if (d < a.rope_dim) {
-                int i, partner;
-                bool first;
-                if (a.interleaved) {
-                    i = d >> 1;
-                    first = (d & 1) == 0;
-                    partner = first ? d + 1 : d - 1;
-                } else {
-                    first = d < half;
-                    i = first ? d : d - half;
-                    partner = first ? d + half : d - half;
+        for (int k = 0; k < NV; ++k) {
+            float4v y = x[k];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int d = 4 * l32 + 128 * k + e;
+                if (d < a.rope_dim) {
+                    int i;
+                    bool first;
+                    float other;
+                    if (a.interleaved) {
+                        i = d >> 1;
+                        first = (d & 1) == 0;
+                        other = first ? x[k][e + 1 < 4 ? e + 1 : e] : x[k][e > 0 ? e - 1 : e];
+                    } else {
+                        first = d < half;
+                        i = first ? d : d - half;
+                        other = s_x[half_id][first ? d + half : d - half];
+                    }
+                    // angle = pos * theta^(-2i/rope_dim), reduced modulo 2 pi in fp64
+                    const double ang = (double)pos64 * a.inv_freq[i];
+                    const double red = ang - kTwoPi * floor(ang * kInvTwoPi);
+                    float sn, cs;
+                    sincosf((float)red, &sn, &cs);
+                    y[e] = first ? x[k][e] * cs - other * sn : other * sn + x[k][e] * cs;
                 }
-                // angle = pos * theta^(-2i/rope_dim), reduced modulo 2 pi in fp64
-                const double ang = (double)pos64 * a.inv_freq[i];
-                const double red = ang - kTwoPi * floor(ang * kInvTwoPi);
-                float sn, cs;
-                sincosf((float)red, &sn, &cs);
-                const float other = s_x[wave][partner];
-                x[k] = first ? x[k] * cs - other * sn : other * sn + x[k] * cs;
             }
+            x[k] = y;
         }
     }
+    if (!act) return;
 
     if (is_q) {
         float *dst = a.q_out + b * a.qo_bs + (int64_t)t * a.qo_ts + (int64_t)head * a.qo_hs;
 #pragma unroll
-        for (int k = 0; k < PER; ++k) dst[lane + 64 * k] = x[k];
+        for (int k = 0; k < NV; ++k) *reinterpret_cast<float4v *>(dst + 4 * l32 + 128 * k) = x[k];
         return;
     }
     const int pos = (int)pos64;  // below ctx_cap here
@@ -141,8 +161,13 @@ __global__ __launch_bounds__(256) void prepare_kernel(PrepareArgs a) {
     uint16_t *dst = pool + (int64_t)page * a.page_stride + (int64_t)(pos - pg * a.page_size) * a.token_stride +
                     (int64_t)head * a.head_stride;
 #pragma unroll
-    for (int k = 0; k < PER; ++k)
-        dst[lane + 64 * k] = a.bf16 ? f32_to_bf16_rne(x[k]) : __builtin_bit_cast(uint16_t, (_Float16)x[k]);
+    for (int k = 0; k < NV; ++k) {
+        uint16_t h[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            h[e] = a.bf16 ? f32_to_bf16_rne(x[k][e]) : __builtin_bit_cast(uint16_t, (_Float16)x[k][e]);
+        *reinterpret_cast<uint2 *>(dst + 4 * l32 + 128 * k) = make_uint2(pack2(h[0], h[1]), pack2(h[2], h[3]));
+    }
 }
 
 }  // namespace
@@ -201,7 +226,7 @@ hipError_t launch_paged_prepare(const attn_paged_prepare_params *p, const float 
     for (int i = 0; i < kPrepareMaxPairs; ++i)
         a.inv_freq[i] = i < p->rope_dim / 2 ? exp2(-log2_theta * (2.0 * i) / (double)p->rope_dim) : 0.0;
     const int64_t items = (int64_t)p->batch * p->max_tokens * (p->n_heads + 2 * p->n_kv_heads);
-    const dim3 grid((unsigned)((items + 3) / 4));
+    const dim3 grid((unsigned)((items + 7) / 8));  // eight half-wave items per workgroup
     switch (p->head_dim) {
     case 128: hipLaunchKernelGGL((prepare_kernel<128>), grid, dim3(256), 0, stream, a); break;
     case 256: hipLaunchKernelGGL((prepare_kernel<256>), grid, dim3(256), 0, stream, a); break;

@@ -225,7 +225,10 @@ int attn_paged_prefill(const attn_paged_prefill_params *p, const float *q, const
  * Raw projections are F32 [batch, max_tokens, heads, >= head_dim] with
  * strides (bs, ts, hs); a query head stride of 2*head_dim leaves an output
  * gate half untouched.  Norm weights are F32.  head_dim 128 or 256;
- * 0 < rope_dim <= head_dim, rope_dim even ([paged] shape rules).
+ * 0 < rope_dim <= head_dim, rope_dim even ([paged] shape rules).  Rows are
+ * read and written 16 bytes at a time: the F32 buffers 16-byte aligned, the
+ * pools 8-byte aligned, every stride a multiple of 4 elements (ATTN_EINVAL
+ * otherwise).
  * ---------------------------------------------------------------------- */
 typedef struct {
     int32_t batch, n_heads, n_kv_heads, head_dim, max_tokens;

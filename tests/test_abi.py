@@ -316,12 +316,22 @@ def _prepare(**kw):
     (dict(head_dim=64), b"head_dim"), (dict(n_kv_heads=3), b"multiple"), (dict(kv_dtype=_ffi.ATTN_F32), b"kv_dtype"),
     (dict(rope_theta=0.0), b"rope_theta"), (dict(epsilon=-1.0), b"epsilon"), (dict(qr_cap=100), b"q_raw holds"),
     (dict(qn_hs=128), b"norm weights"), (dict(kv_cap=100), b"KV pools"), (dict(max_tokens=0), b"shape"),
+    (dict(qr_hs=130, qr_cap=1 << 20), b"multiples of 4"), (dict(kv_token_stride=2 * 128 + 2), b"multiples of 4"),
 ])
 def test_prepare_rejects_before_launch(lib, kw, msg):
     fake = 1 << 20  # never dereferenced: the call must fail in host validation
     p = _prepare(**kw)
     assert lib.attn_paged_prepare(ctypes.byref(p), *([fake] * 11), None) == _ffi.ATTN_EINVAL
     assert msg in lib.attn_last_error(), lib.attn_last_error()
+
+
+def test_prepare_rejects_unaligned_rows(lib):
+    fake = 1 << 20
+    p = _prepare()
+    args = [fake] * 11
+    args[0] = fake + 4  # q_raw 4-byte but not 16-byte aligned
+    assert lib.attn_paged_prepare(ctypes.byref(p), *args, None) == _ffi.ATTN_EINVAL
+    assert b"aligned" in lib.attn_last_error()
 
 
 def test_prepare_needs_norm_weights_when_asked(lib):
